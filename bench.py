@@ -1,0 +1,181 @@
+"""Benchmark: attention forward + backward TFLOP/s (unmasked FLOPs) on one MI355X.
+
+One step = one pass of the whole path over one batch of synthetic input:
+attn_fwd, attn_bwd_preprocess, attn_bwd_dq, attn_bwd_dkv.  FLOPs count only
+visible (query, key) pairs (exact count from attn_plan_count):
+forward 4 D per pair per query head, backward 10 D.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 5]
+                    [--no-cpu-baseline] [--precise-ds 0|1]
+
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "attention fwd+bwd TFLOP/s (unmasked FLOPs) and % bf16 MFMA peak, 1 GPU"
+PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA (256 CU x 2.4 GHz x 4096 flop/clk/CU)
+PEAK_F32_TFLOPS = 157.3        # fp32 (matrix and vector)
+HBM_GBPS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=5, help="workload number 1..5")
+    ap.add_argument("--precise-ds", type=int, default=1)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-len", type=int, default=3072,
+                    help="prefix length of the oracle's bounded sample")
+    return ap.parse_args()
+
+
+def cpu_baseline(w, sample_len: int):
+    """The fp64 oracle, as is, on a bounded sample of the workload: batch 0,
+    query head 0 (its KV head), the first `sample_len` positions, forward and
+    backward.  Rate = counted FLOPs of that sample / wall time."""
+    import numpy as np
+    from oracle import Params, backward, unmasked_pairs
+    from workloads import make_inputs, to_f64, to_i32
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+    ws = w.scaled(L=min(sample_len, w.L), B=1, Hq=1, Hkv=1)
+    inp = make_inputs(ws)
+    q, k, v, do = (to_f64(inp[n]) for n in ("q", "k", "v", "do"))
+    temp, seg, rb = to_f64(inp["temperature"]), to_i32(inp["segment_ids"]), to_i32(inp["ranker_bounds"])
+    p = Params(w.sm_scale, w.causal, w.window_len, w.cap_method, w.cap, w.alpha, w.beta,
+               w.z_loss_weight)
+    t0 = time.perf_counter()
+    backward(q, k, v, do, p, temp, seg, rb)
+    dt = time.perf_counter() - t0
+    pairs = unmasked_pairs(ws.L, p, seg, rb, B=1)
+    flops = 14.0 * w.D * pairs
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"batch 0, head 0, first {ws.L} positions of the workload, fwd+bwd in fp64 "
+                      f"({pairs} visible pairs, {dt:.1f} s)",
+            "seconds": dt}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import torch
+    import blockwise_softmax_attention_amd as ba
+    from workloads import WORKLOADS, make_inputs
+
+    torch.cuda.set_device(0)
+    w = WORKLOADS[args.workload]
+    inp = make_inputs(w)
+    dev = {k: (v.cuda() if v is not None else None) for k, v in inp.items()}
+    p = ba.params_for(w, precise_ds=bool(args.precise_ds))
+    pairs, tiles = ba.attn_plan_count(p, inp["segment_ids"], inp["ranker_bounds"])
+    fwd_flop = 4.0 * w.D * pairs
+    bwd_flop = 10.0 * w.D * pairs
+
+    B, L, Hq, Hkv, D = w.B, w.L, w.Hq, w.Hkv, w.D
+    f32 = dict(dtype=torch.float32, device="cuda")
+    o = torch.empty((B, L, Hq, D), **f32)
+    m = torch.empty((B, Hq, L), **f32)
+    l = torch.empty((B, Hq, L), **f32)
+    delta = torch.empty((B, Hq, L), **f32)
+    dq = torch.empty((B, L, Hq, D), **f32)
+    dk = torch.empty((B, L, Hkv, D), **f32)
+    dv = torch.empty((B, L, Hkv, D), **f32)
+    q, k, v, do = dev["q"], dev["k"], dev["v"], dev["do"]
+    temp, seg, rb = dev["temperature"], dev["segment_ids"], dev["ranker_bounds"]
+    stream = torch.cuda.current_stream()
+
+    names = ["attn_fwd", "attn_bwd_preprocess", "attn_bwd_dq", "attn_bwd_dkv"]
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        ba.attn_fwd(p, q, k, v, temp, seg, rb, o, m, l, stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+        ba.attn_bwd_preprocess(p, o, do, delta, stream=stream)
+        if ev is not None:
+            ev[2].record(stream)
+        ba.attn_bwd_dq(p, q, k, v, do, m, l, delta, temp, seg, rb, dq, stream=stream)
+        if ev is not None:
+            ev[3].record(stream)
+        ba.attn_bwd_dkv(p, q, k, v, do, m, l, delta, temp, seg, rb, dk, dv, stream=stream)
+        if ev is not None:
+            ev[4].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    per = {n: [] for n in names}
+    for e in evs:
+        for j, n in enumerate(names):
+            per[n].append(e[j].elapsed_time(e[j + 1]))
+    avg = {n: sum(x) / len(x) for n, x in per.items()}
+    step_ms = wall * 1e3 / args.steps
+    fwd_ms = avg["attn_fwd"]
+    bwd_ms = avg["attn_bwd_preprocess"] + avg["attn_bwd_dq"] + avg["attn_bwd_dkv"]
+    value = (fwd_flop + bwd_flop) / (step_ms * 1e-3) / 1e12
+    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
+
+    # Roofline of the dominant kernel: algorithmic MFMA FLOPs per launch over its
+    # average duration (HIP events on the launch stream, timed region only).
+    # Per visible pair and query head: fwd 4 D (QK^T, PV); dq 6 D (QK^T, dO V^T,
+    # dS K); dkv 8 D (QK^T, dO V^T, P^T dO, dS^T Q).  Preprocess is HBM-bound:
+    # reads O (f32) and dO, writes delta.
+    alg = {"attn_fwd": 4.0 * D * pairs, "attn_bwd_dq": 6.0 * D * pairs,
+           "attn_bwd_dkv": 8.0 * D * pairs}
+    dom = max(alg, key=lambda n: avg[n])
+    achieved = alg[dom] / (avg[dom] * 1e-3) / 1e12
+    pre_bytes = B * L * Hq * D * (4 + (2 if w.dtype == "bf16" else 4)) + B * Hq * L * 4
+    roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2),
+                "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None}
+
+    out = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": w.name, "batch": B, "seq_len": L, "q_heads": Hq, "kv_heads": Hkv,
+                   "head_dim": D, "cap": w.cap_method, "causal": w.causal, "window": w.window_len,
+                   "precise_ds": bool(args.precise_ds), "visible_pairs": pairs},
+        "pct_peak": round(100.0 * value / peak, 2),
+        "fwd": {"ms": round(fwd_ms, 4), "tflops": round(fwd_flop / (fwd_ms * 1e-3) / 1e12, 2),
+                "pct_peak": round(100.0 * fwd_flop / (fwd_ms * 1e-3) / 1e12 / peak, 2)},
+        "bwd": {"ms": round(bwd_ms, 4), "tflops": round(bwd_flop / (bwd_ms * 1e-3) / 1e12, 2),
+                "pct_peak": round(100.0 * bwd_flop / (bwd_ms * 1e-3) / 1e12 / peak, 2)},
+        "kernels_ms": {n: round(avg[n], 4) for n in names},
+        "preprocess_gbps": round(pre_bytes / (avg["attn_bwd_preprocess"] * 1e-3) / 1e9, 1),
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_sample_len)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,235 @@
+"""Thin Python binding of libattn.so (blockwise online-softmax attention, gfx950).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI declared in include/attn.h.  PyTorch provides device
+memory and the current HIP stream.  There is no fallback: if the library is
+missing or the tensors are not on the GPU, the calls raise.
+
+Names mirror the C ABI: attn_fwd, attn_bwd_preprocess, attn_bwd_dq,
+attn_bwd_dkv, attn_plan_count, attn_check_params.
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import os
+from typing import Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libattn.so")
+
+ATTN_F32, ATTN_BF16 = 0, 1
+CAP_CODES = {"none": 0, "tanh": 1, "soft_sign": 2, "alsc": 3}
+STATUS_NAMES = {0: "ATTN_OK", -1: "ATTN_ERR_NULL_PTR", -2: "ATTN_ERR_SHAPE", -3: "ATTN_ERR_DTYPE",
+                -4: "ATTN_ERR_UNSUPPORTED", -5: "ATTN_ERR_ALIGN", -6: "ATTN_ERR_PARAM",
+                -7: "ATTN_ERR_HIP"}
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        self.status = status
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {detail}")
+
+
+class _CParams(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("seq_len", ctypes.c_int32),
+                ("q_heads", ctypes.c_int32), ("kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("sm_scale", ctypes.c_float), ("causal", ctypes.c_int32),
+                ("window_len", ctypes.c_int32), ("cap_method", ctypes.c_int32),
+                ("cap", ctypes.c_float), ("alpha", ctypes.c_float), ("beta", ctypes.c_float),
+                ("z_loss_weight", ctypes.c_float), ("precise_ds", ctypes.c_int32)]
+
+
+@dataclasses.dataclass
+class AttnParams:
+    batch: int
+    seq_len: int
+    q_heads: int
+    kv_heads: int
+    head_dim: int
+    dtype: int = ATTN_BF16
+    sm_scale: float = 1.0
+    causal: bool = False
+    window_len: int = 0
+    cap_method: int = 0
+    cap: float = 0.0
+    alpha: float = 0.0
+    beta: float = 0.0
+    z_loss_weight: float = 0.0
+    precise_ds: bool = True
+
+    def to_c(self) -> _CParams:
+        return _CParams(int(self.batch), int(self.seq_len), int(self.q_heads), int(self.kv_heads),
+                        int(self.head_dim), int(self.dtype), float(self.sm_scale),
+                        int(bool(self.causal)), int(self.window_len), int(self.cap_method),
+                        float(self.cap), float(self.alpha), float(self.beta),
+                        float(self.z_loss_weight), int(bool(self.precise_ds)))
+
+
+_lib = None
+_P = ctypes.c_void_p
+_FN_SIGS = {
+    "attn_fwd": [ctypes.POINTER(_CParams), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
+    "attn_bwd_preprocess": [ctypes.POINTER(_CParams), _P, _P, _P, _P],
+    "attn_bwd_dq": [ctypes.POINTER(_CParams), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
+    "attn_bwd_dkv": [ctypes.POINTER(_CParams), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
+    "attn_plan_count": [ctypes.POINTER(_CParams), _P, _P, ctypes.POINTER(ctypes.c_int64),
+                        ctypes.POINTER(ctypes.c_int64)],
+    "attn_check_params": [ctypes.POINTER(_CParams)],
+}
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libattn.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} not found: build it with "
+                           "`python -m blockwise_softmax_attention_amd.build`")
+    lib = ctypes.CDLL(path)
+    for name, args in _FN_SIGS.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = ctypes.c_int
+    for name in ("attn_status_str", "attn_last_error", "attn_build_info"):
+        getattr(lib, name).restype = ctypes.c_char_p
+    lib.attn_status_str.argtypes = [ctypes.c_int]
+    _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status != 0:
+        raise AttnError(status, load_library().attn_last_error().decode())
+
+
+def _ptr(t: Optional[torch.Tensor], name: str, dtype=None, device_required=True):
+    if t is None:
+        return None
+    if device_required and t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _in_dtype(p: AttnParams):
+    return torch.bfloat16 if p.dtype == ATTN_BF16 else torch.float32
+
+
+def attn_check_params(p: AttnParams) -> None:
+    cp = p.to_c()
+    _check(load_library().attn_check_params(ctypes.byref(cp)))
+
+
+def attn_fwd(p: AttnParams, q, k, v, temperature=None, segment_ids=None, ranker_bounds=None,
+             o=None, m=None, l=None, stream=None):
+    """Returns (o, m, l); allocates the outputs it is not given."""
+    B, L, Hq, D = p.batch, p.seq_len, p.q_heads, p.head_dim
+    dev = q.device
+    o = torch.empty((B, L, Hq, D), dtype=torch.float32, device=dev) if o is None else o
+    m = torch.empty((B, Hq, L), dtype=torch.float32, device=dev) if m is None else m
+    l = torch.empty((B, Hq, L), dtype=torch.float32, device=dev) if l is None else l
+    dt = _in_dtype(p)
+    cp = p.to_c()
+    _check(load_library().attn_fwd(
+        ctypes.byref(cp), _ptr(q, "q", dt), _ptr(k, "k", dt), _ptr(v, "v", dt),
+        _ptr(temperature, "temperature", torch.float32), _ptr(segment_ids, "segment_ids", torch.int32),
+        _ptr(ranker_bounds, "ranker_bounds", torch.int32), _ptr(o, "o", torch.float32),
+        _ptr(m, "m", torch.float32), _ptr(l, "l", torch.float32), _stream(stream)))
+    return o, m, l
+
+
+def attn_bwd_preprocess(p: AttnParams, o, d_o, delta=None, stream=None):
+    delta = torch.empty((p.batch, p.q_heads, p.seq_len), dtype=torch.float32,
+                        device=o.device) if delta is None else delta
+    cp = p.to_c()
+    _check(load_library().attn_bwd_preprocess(
+        ctypes.byref(cp), _ptr(o, "o", torch.float32), _ptr(d_o, "d_o", _in_dtype(p)),
+        _ptr(delta, "delta", torch.float32), _stream(stream)))
+    return delta
+
+
+def attn_bwd_dq(p: AttnParams, q, k, v, d_o, m, l, delta, temperature=None, segment_ids=None,
+                ranker_bounds=None, dq=None, stream=None):
+    dq = torch.empty((p.batch, p.seq_len, p.q_heads, p.head_dim), dtype=torch.float32,
+                     device=q.device) if dq is None else dq
+    dt = _in_dtype(p)
+    cp = p.to_c()
+    _check(load_library().attn_bwd_dq(
+        ctypes.byref(cp), _ptr(q, "q", dt), _ptr(k, "k", dt), _ptr(v, "v", dt),
+        _ptr(temperature, "temperature", torch.float32), _ptr(segment_ids, "segment_ids", torch.int32),
+        _ptr(ranker_bounds, "ranker_bounds", torch.int32), _ptr(d_o, "d_o", dt),
+        _ptr(m, "m", torch.float32), _ptr(l, "l", torch.float32), _ptr(delta, "delta", torch.float32),
+        _ptr(dq, "dq", torch.float32), _stream(stream)))
+    return dq
+
+
+def attn_bwd_dkv(p: AttnParams, q, k, v, d_o, m, l, delta, temperature=None, segment_ids=None,
+                 ranker_bounds=None, dk=None, dv=None, stream=None):
+    shape = (p.batch, p.seq_len, p.kv_heads, p.head_dim)
+    dk = torch.empty(shape, dtype=torch.float32, device=q.device) if dk is None else dk
+    dv = torch.empty(shape, dtype=torch.float32, device=q.device) if dv is None else dv
+    dt = _in_dtype(p)
+    cp = p.to_c()
+    _check(load_library().attn_bwd_dkv(
+        ctypes.byref(cp), _ptr(q, "q", dt), _ptr(k, "k", dt), _ptr(v, "v", dt),
+        _ptr(temperature, "temperature", torch.float32), _ptr(segment_ids, "segment_ids", torch.int32),
+        _ptr(ranker_bounds, "ranker_bounds", torch.int32), _ptr(d_o, "d_o", dt),
+        _ptr(m, "m", torch.float32), _ptr(l, "l", torch.float32), _ptr(delta, "delta", torch.float32),
+        _ptr(dk, "dk", torch.float32), _ptr(dv, "dv", torch.float32), _stream(stream)))
+    return dk, dv
+
+
+def attn_plan_count(p: AttnParams, segment_ids=None, ranker_bounds=None):
+    """(unmasked pairs, visited forward tiles), both summed over batch and heads.
+    Host-side; segment_ids / ranker_bounds are CPU int32 tensors or None."""
+    import numpy as np
+
+    def host(t):
+        if t is None:
+            return None, None
+        a = np.ascontiguousarray(t.cpu().numpy() if isinstance(t, torch.Tensor) else t, dtype=np.int32)
+        return a, a.ctypes.data
+
+    seg, seg_p = host(segment_ids)
+    rb, rb_p = host(ranker_bounds)
+    pairs, tiles = ctypes.c_int64(0), ctypes.c_int64(0)
+    cp = p.to_c()
+    _check(load_library().attn_plan_count(ctypes.byref(cp), seg_p, rb_p, ctypes.byref(pairs),
+                                          ctypes.byref(tiles)))
+    del seg, rb
+    return pairs.value, tiles.value
+
+
+def attention_forward_backward(p: AttnParams, q, k, v, d_o, temperature=None, segment_ids=None,
+                               ranker_bounds=None, stream=None):
+    """One pass of the whole path: forward, then preprocess, dQ and dK/dV."""
+    o, m, l = attn_fwd(p, q, k, v, temperature, segment_ids, ranker_bounds, stream=stream)
+    delta = attn_bwd_preprocess(p, o, d_o, stream=stream)
+    dq = attn_bwd_dq(p, q, k, v, d_o, m, l, delta, temperature, segment_ids, ranker_bounds,
+                     stream=stream)
+    dk, dv = attn_bwd_dkv(p, q, k, v, d_o, m, l, delta, temperature, segment_ids, ranker_bounds,
+                          stream=stream)
+    return dict(o=o, m=m, l=l, delta=delta, dq=dq, dk=dk, dv=dv)
+
+
+def params_for(w, precise_ds: bool = True) -> AttnParams:
+    """AttnParams of a workloads.Workload description."""
+    return AttnParams(batch=w.B, seq_len=w.L, q_heads=w.Hq, kv_heads=w.Hkv, head_dim=w.D,
+                      dtype=ATTN_BF16 if w.dtype == "bf16" else ATTN_F32, sm_scale=w.sm_scale,
+                      causal=w.causal, window_len=w.window_len,
+                      cap_method=CAP_CODES[w.cap_method], cap=w.cap, alpha=w.alpha, beta=w.beta,
+                      z_loss_weight=w.z_loss_weight, precise_ds=precise_ds)

@@ -1,0 +1,64 @@
+// Host/device shared definitions: kernel argument block, tile sizes, launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attn {
+
+// Tile geometry.  A workgroup of 4 waves (256 threads) owns BM_FWD query rows
+// (32 per wave) in the forward and dQ kernels, and 32 * DKV_WAVES keys in the
+// dK/dV kernel; key tiles (forward, dQ) and query tiles (dK/dV) stream through
+// LDS in steps of BN rows.
+constexpr int NWAVES = 4;
+constexpr int NTHREADS = 64 * NWAVES;
+constexpr int BM = 32 * NWAVES;          // query rows per forward / dQ workgroup
+constexpr int BKV = 32 * NWAVES;         // key rows per dK/dV workgroup
+constexpr int MAX_TILES = 4096;          // segment-skip flags per workgroup (key or query tiles)
+
+// Kernel argument block (passed by value).
+struct KArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* dout;
+  const float* temp;       // (B, L) or null
+  const int32_t* seg;      // (B, L) or null
+  const int32_t* bounds;   // (B, 4) or null
+  const float* o_in;       // preprocess: O
+  const float* m_in;       // backward: m, l, delta (B, Hq, L)
+  const float* l_in;
+  const float* delta_in;
+  float* out0;             // fwd: O      dq: dQ    dkv: dK   pre: delta
+  float* out1;             // fwd: m                dkv: dV
+  float* out2;             // fwd: l
+  int B, L, Hq, Hkv, G;
+  int causal, window;
+  float sm_scale;
+  float zw;                // z-loss weight
+  // Cap constants.  For a raw dot product x = <q, k> and a row with
+  // temperature t, the log2-domain logit minus the row's log2 LSE is
+  //   fma(f(x), kmul * t, kadd * t - lse2)
+  // where f depends on the cap (see Cap<> in attn_device.h), and
+  //   cap'(sm_scale x) * sm_scale * t = rmul * t * g(x).
+  float kmul, kadd, rmul;
+  float cx;                // coefficient of x inside exp2 / the soft-sign denominator
+  float cb;                // additive exponent term (alsc)
+  float acc_a;             // float path, alsc: exp(-alpha beta)
+  float acc_inv_cap;       // float path: sm_scale / cap
+  float acc_alpha_beta;    // float path, alsc: alpha * beta
+  float acc_u;             // float path, alsc: alpha * sm_scale / cap
+  int precise_ds;
+  int n_items;             // workgroups doing real work
+  int n_q_tiles;           // ceil(L / BM)
+  int n_kv_tiles;          // ceil(L / BKV)
+};
+
+// Launchers (one per kernel family); dtype 0 = f32, 1 = bf16; cap 0..3.
+hipError_t launch_fwd(const KArgs& a, int dtype, int head_dim, int cap, hipStream_t s);
+hipError_t launch_preprocess(const KArgs& a, int dtype, int head_dim, hipStream_t s);
+hipError_t launch_dq(const KArgs& a, int dtype, int head_dim, int cap, hipStream_t s);
+hipError_t launch_dkv(const KArgs& a, int dtype, int head_dim, int cap, hipStream_t s);
+int fwd_key_tile(int dtype, int head_dim);   // keys per forward tile
+
+}  // namespace attn

@@ -1,0 +1,119 @@
+// Tile classification shared by the kernels and the host planner.
+//
+// The visibility rule of one (query i, key j) pair is the AND of the enabled
+// predicates (triton_kernels.py page, forward kernel: segment equality,
+// i >= j, j > i - W; mosaic_backward.py page, ranker_mask_mosaic_kv_q:
+// (j in hist and (i in hist or i in cand)) or (i in cand and j == i)).
+// Which tiles to visit is derived here from those element predicates, so a
+// tile is skipped only if it holds no visible pair, and every tile is visited
+// at most once, whatever the tile sizes, window length or ranker split.
+#pragma once
+
+#if defined(__HIPCC__)
+#define ATTN_HD __host__ __device__ inline
+#else
+#define ATTN_HD inline
+#endif
+
+namespace attn {
+
+enum TileClass { TILE_EMPTY = 0, TILE_FULL = 1, TILE_PARTIAL = 2 };
+
+struct MaskSpec {
+  int L;
+  int causal;
+  int window;           // 0: off
+  int ranker;           // 0: off
+  int hl, hu, cl, cu;   // ranker bounds of this batch row
+  int has_seg;          // segment ids present (tiles with them are never FULL)
+};
+
+ATTN_HD int imin(int a, int b) { return a < b ? a : b; }
+ATTN_HD int imax(int a, int b) { return a > b ? a : b; }
+
+// Interval [a0, a1) intersects [b0, b1)?
+ATTN_HD bool overlaps(int a0, int a1, int b0, int b1) { return imax(a0, b0) < imin(a1, b1); }
+// [a0, a1) contained in [b0, b1)?
+ATTN_HD bool inside(int a0, int a1, int b0, int b1) { return a0 >= b0 && a1 <= b1; }
+
+// Element predicate without segments.
+ATTN_HD bool pair_visible(int i, int j, const MaskSpec& s) {
+  bool ok = (i < s.L) && (j < s.L) && (i >= 0) && (j >= 0);
+  if (s.causal) ok = ok && (j <= i);
+  if (s.window > 0) ok = ok && (j > i - s.window);
+  if (s.ranker) {
+    bool qh = i >= s.hl && i < s.hu, qc = i >= s.cl && i < s.cu;
+    bool kh = j >= s.hl && j < s.hu, kc = j >= s.cl && j < s.cu;
+    ok = ok && ((kh && (qh || qc)) || (qc && kc && i == j));
+  }
+  return ok;
+}
+
+// Class of the block rows [q0, q1) x keys [k0, k1) under causal / window /
+// ranker / length, ignoring segment ids (the caller handles those).  EMPTY is
+// exact for each predicate alone and therefore sound for their AND; FULL is
+// only returned when every pair is visible.
+ATTN_HD int tile_class(int q0, int q1, int k0, int k1, const MaskSpec& s) {
+  q1 = imin(q1, s.L);
+  k1 = imin(k1, s.L);
+  if (q0 >= q1 || k0 >= k1) return TILE_EMPTY;
+  bool full = true;
+  if (s.causal) {
+    if (k0 > q1 - 1) return TILE_EMPTY;          // every key after every row
+    full = full && (k1 - 1 <= q0);
+  }
+  if (s.window > 0) {
+    if (k1 - 1 < q0 - s.window + 1) return TILE_EMPTY;   // every key too old
+    full = full && (k0 >= (q1 - 1) - s.window + 1);
+  }
+  if (s.ranker) {
+    bool rows_active = overlaps(q0, q1, s.hl, s.hu) || overlaps(q0, q1, s.cl, s.cu);
+    bool hist_pairs = rows_active && overlaps(k0, k1, s.hl, s.hu);
+    // diagonal pairs: i == j in rows, keys and candidates
+    int d0 = imax(imax(q0, k0), s.cl), d1 = imin(imin(q1, k1), s.cu);
+    bool diag_pairs = d0 < d1;
+    if (!hist_pairs && !diag_pairs) return TILE_EMPTY;
+    bool rows_all_active;
+    if (inside(q0, q1, s.hl, s.hu) || inside(q0, q1, s.cl, s.cu)) {
+      rows_all_active = true;
+    } else if (s.hl <= s.cl && s.cl <= s.hu) {
+      rows_all_active = inside(q0, q1, s.hl, imax(s.hu, s.cu));
+    } else if (s.cl <= s.hl && s.hl <= s.cu) {
+      rows_all_active = inside(q0, q1, s.cl, imax(s.hu, s.cu));
+    } else {
+      rows_all_active = false;
+    }
+    full = full && rows_all_active && inside(k0, k1, s.hl, s.hu);
+  }
+  if (s.has_seg) full = false;
+  return full ? TILE_FULL : TILE_PARTIAL;
+}
+
+// Contiguous range of key tiles (tile size bn) that can hold a visible pair
+// for rows [q0, q1): causal and window bounds only.  Returns false if empty.
+ATTN_HD bool key_tile_range(int q0, int q1, int bn, const MaskSpec& s, int* t0, int* t1) {
+  q1 = imin(q1, s.L);
+  if (q0 >= q1) return false;
+  int kmin = 0, kmax = s.L - 1;
+  if (s.window > 0) kmin = imax(kmin, q0 - s.window + 1);
+  if (s.causal) kmax = imin(kmax, q1 - 1);
+  if (kmin > kmax) return false;
+  *t0 = kmin / bn;
+  *t1 = kmax / bn + 1;
+  return true;
+}
+
+// Contiguous range of query tiles (tile size bm) that can see keys [k0, k1).
+ATTN_HD bool query_tile_range(int k0, int k1, int bm, const MaskSpec& s, int* t0, int* t1) {
+  k1 = imin(k1, s.L);
+  if (k0 >= k1) return false;
+  int qmin = 0, qmax = s.L - 1;
+  if (s.causal) qmin = imax(qmin, k0);
+  if (s.window > 0) qmax = imin(qmax, (k1 - 1) + s.window - 1);
+  if (qmin > qmax) return false;
+  *t0 = qmin / bm;
+  *t1 = qmax / bm + 1;
+  return true;
+}
+
+}  // namespace attn

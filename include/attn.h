@@ -1,0 +1,152 @@
+/*
+ * Blockwise online-softmax attention for AMD Instinct MI355X (gfx950): C ABI.
+ *
+ * Self-attention over packed rows, with an optional logit cap, per-query
+ * temperature, segment / causal / sliding-window / ranker masks, grouped-query
+ * heads, and the exact backward pass (plus an optional z-loss term).
+ *
+ * What is computed (web pages on unified blockwise attention):
+ *   - triton_kernels.py page, make_triton_forward_kernel: s = sm_scale q.k,
+ *     segment-equality, causal (i >= j) and window (j > i - W) predicates,
+ *     online softmax with the (l, m) residuals;
+ *   - mosaic_backward.py page, _apply_cap_mosaic: the caps
+ *       none : s             tanh : cap tanh(s/cap)     soft_sign : s/(1+|s|/cap)
+ *       alsc : cap (sig(a(s/cap+b)) - sig(ab)) / (sig(ab)(1-sig(ab)) + 1e-12);
+ *   - triton_kernels.py page (dq and dkv kernels) and the module docstring of
+ *     the mosaic_backward.py page: the backward chain
+ *       dP = dO V^T, dS' = P (dP - delta) + w P LSE,
+ *       dS = dS' temp cap'(s) sm_scale, dQ = dS K, dK = dS^T Q, dV = P^T dO;
+ *   - mosaic_backward.py page, ranker_mask_mosaic_kv_q: the ranker mask;
+ *   - mosaic_backward.py page, make_mosaic_backward_dq_kernel: the GQA map
+ *     kv_head = q_head / (Hq / Hkv), dK and dV summed over each group.
+ *
+ * Definitions used here for every row i of (batch b, query head h), with
+ * g = h / (Hq/Hkv):
+ *   S'_ij = temp[b,i] * cap(sm_scale * <Q[b,i,h,:], K[b,j,g,:]>)   (visible j)
+ *   m_i = max_j S'_ij,  l_i = sum_j exp(S'_ij - m_i),  LSE_i = m_i + ln l_i
+ *   P_ij = exp(S'_ij - LSE_i) (0 for masked pairs),  O_i = sum_j P_ij V_j
+ *   The backward is the gradient of sum(O * dO) + (w/2) sum_i LSE_i^2.
+ *   A row that sees no key has O = 0, m = -inf, l = 0 and no gradient.
+ *   The ALSC derivative is the exact one, a sig(z)(1-sig(z))/denom.
+ *
+ * Layouts (all contiguous, row-major, device memory):
+ *   Q, dO, O, dQ : (B, L, Hq, D)      K, V, dK, dV : (B, L, Hkv, D)
+ *   m, l, delta  : (B, Hq, L) float   temperature  : (B, L) float
+ *   segment_ids  : (B, L) int32       ranker_bounds: (B, 4) int32 = hl, hu, cl, cu
+ *   Q, K, V, dO are float or bfloat16 (params.dtype); O, m, l, delta, dQ, dK,
+ *   dV are always float.
+ *
+ * Ownership: the caller allocates and owns every buffer; the library keeps
+ * no state between calls and allocates no device memory.  Every compute call
+ * only enqueues kernels on `stream` (a hipStream_t; NULL = default stream) and
+ * returns; the caller synchronises.  Outputs are overwritten, never
+ * accumulated, and no call uses atomics: results are bitwise reproducible.
+ *
+ * Ranker bounds and segment ids may hold any int32 values: they only enter
+ * the visibility predicates, never an address.
+ *
+ * Errors: every argument is validated on the host before any launch; on a
+ * non-OK status nothing was enqueued, and attn_last_error() returns a
+ * thread-local message.  A launch failure reported by the HIP runtime returns
+ * ATTN_ERR_HIP.
+ */
+#ifndef BLOCKWISE_ATTN_H
+#define BLOCKWISE_ATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  ATTN_OK = 0,
+  ATTN_ERR_NULL_PTR = -1,    /* a required pointer is NULL */
+  ATTN_ERR_SHAPE = -2,       /* a size is < 1 (L, B, heads) or too large */
+  ATTN_ERR_DTYPE = -3,       /* dtype is neither ATTN_F32 nor ATTN_BF16 */
+  ATTN_ERR_UNSUPPORTED = -4, /* head_dim not 64 or 128, or Hq not a multiple of Hkv */
+  ATTN_ERR_ALIGN = -5,       /* a tensor pointer is not 16-byte aligned */
+  ATTN_ERR_PARAM = -6,       /* unknown cap, window < 0, z-loss < 0, sm_scale <= 0,
+                                or a non-finite scalar parameter */
+  ATTN_ERR_HIP = -7          /* the HIP runtime reported an error at launch */
+} attn_status;
+
+typedef enum {
+  ATTN_CAP_NONE = 0,
+  ATTN_CAP_TANH = 1,
+  ATTN_CAP_SOFT_SIGN = 2,
+  ATTN_CAP_ALSC = 3
+} attn_cap;
+
+typedef enum { ATTN_F32 = 0, ATTN_BF16 = 1 } attn_dtype;
+
+typedef struct {
+  int32_t batch;        /* B >= 1 */
+  int32_t seq_len;      /* L >= 1, <= ATTN_MAX_SEQ_LEN; queries and keys share it */
+  int32_t q_heads;      /* Hq >= 1 */
+  int32_t kv_heads;     /* Hkv >= 1, Hq % Hkv == 0 */
+  int32_t head_dim;     /* D: 64 or 128 */
+  int32_t dtype;        /* attn_dtype of Q, K, V, dO */
+  float sm_scale;       /* > 0 */
+  int32_t causal;       /* nonzero: key j visible from row i only if j <= i */
+  int32_t window_len;   /* 0: off; else key j visible only if j > i - window_len */
+  int32_t cap_method;   /* attn_cap; a cap <= 0 means no cap whatever the method */
+  float cap, alpha, beta;
+  float z_loss_weight;  /* w >= 0 */
+  int32_t precise_ds;   /* bf16 only: nonzero rounds dS to a hi+lo pair of bf16
+                           operands for dQ and dK (two MFMAs), zero to one bf16 */
+} attn_params;
+
+#define ATTN_MAX_SEQ_LEN 262144
+/* With segment ids the workgroup-local segment-skip table bounds L further. */
+#define ATTN_MAX_SEQ_LEN_SEGMENTS 131072
+
+/* Forward.  temperature NULL means 1 everywhere; segment_ids NULL means one
+ * segment; ranker_bounds NULL means no ranker mask.  Writes o, m, l. */
+attn_status attn_fwd(const attn_params* params, const void* q, const void* k, const void* v,
+                     const float* temperature, const int32_t* segment_ids,
+                     const int32_t* ranker_bounds, float* o, float* m, float* l,
+                     void* stream);
+
+/* Backward preprocess (mosaic_backward.py page, make_preprocess_backward_kernel):
+ * delta[b,h,i] = sum_d O[b,i,h,d] * dO[b,i,h,d], with the normalised O that
+ * attn_fwd writes. */
+attn_status attn_bwd_preprocess(const attn_params* params, const float* o, const void* d_o,
+                                float* delta, void* stream);
+
+/* dQ (triton_kernels.py page, make_triton_backward_kernel_dq): recomputes P
+ * from m and l and writes dq (B, L, Hq, D). */
+attn_status attn_bwd_dq(const attn_params* params, const void* q, const void* k, const void* v,
+                        const float* temperature, const int32_t* segment_ids,
+                        const int32_t* ranker_bounds, const void* d_o, const float* m,
+                        const float* l, const float* delta, float* dq, void* stream);
+
+/* dK and dV (triton_kernels.py page, make_triton_backward_kernel_dkv), each
+ * summed over the Hq/Hkv query heads of a key/value head inside one
+ * workgroup (no atomics).  Writes dk, dv (B, L, Hkv, D). */
+attn_status attn_bwd_dkv(const attn_params* params, const void* q, const void* k, const void* v,
+                         const float* temperature, const int32_t* segment_ids,
+                         const int32_t* ranker_bounds, const void* d_o, const float* m,
+                         const float* l, const float* delta, float* dk, float* dv,
+                         void* stream);
+
+/* Host only, no GPU needed: exact number of visible (query, key) pairs summed
+ * over batch rows and query heads, and the number of (query tile, key tile)
+ * pairs the forward kernel visits, summed likewise.  segment_ids_host and
+ * ranker_bounds_host are host pointers (or NULL). */
+attn_status attn_plan_count(const attn_params* params, const int32_t* segment_ids_host,
+                            const int32_t* ranker_bounds_host, int64_t* unmasked_pairs,
+                            int64_t* visited_tiles);
+
+/* Host only: validates params as the compute calls do, without any pointer. */
+attn_status attn_check_params(const attn_params* params);
+
+const char* attn_status_str(attn_status status);
+const char* attn_last_error(void);   /* thread-local detail of the last non-OK status */
+const char* attn_build_info(void);   /* tile sizes and target, for logs */
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BLOCKWISE_ATTN_H */

@@ -47,6 +47,7 @@ import dataclasses
 from typing import Optional
 
 import numpy as np
+from scipy.special import expit
 
 CAP_METHODS = ("none", "tanh", "soft_sign", "alsc")
 
@@ -73,13 +74,7 @@ def sigmoid(x):
     The Mosaic page imports ``_sigmoid`` without printing it; the standard
     logistic function is the plain reading.
     """
-    x = np.asarray(x, dtype=np.float64)
-    out = np.empty_like(x)
-    pos = x >= 0
-    out[pos] = 1.0 / (1.0 + np.exp(-x[pos]))
-    ex = np.exp(x[~pos])
-    out[~pos] = ex / (1.0 + ex)
-    return out
+    return expit(np.asarray(x, dtype=np.float64))
 
 
 def _alsc_consts(cap, alpha, beta):
@@ -253,24 +248,36 @@ def _ds_block(st, q, v, do, b, hq, rr, p: Params, delta_rows):
 
 
 def backward(q, k, v, do, p: Params, temperature=None, segment_ids=None, ranker_bounds=None,
-             row_chunk: int = 512):
+             row_chunk: int = 512, groups=None):
     """Gradients of F = sum(O * dO) + (w/2) * sum over rows of LSE^2.
 
     Returns dict(delta (B,Hq,L), dq (B,L,Hq,D), dk, dv (B,L,Hkv,D), o, m, l).
     delta_i = sum_d O_id dO_id; dP = dO V^T; dS as in ``_ds_block``;
     dQ = dS K; dK = sum over the query heads of a group of dS^T Q;
     dV = likewise of P^T dO.
+    ``groups`` restricts the work to a list of (b, kv_head) pairs (every query
+    head of each group); entries outside are left NaN.
     """
     B, L, Hq, Hkv, D, G = _check(q, k, v)
-    o, m, l = forward(q, k, v, p, temperature, segment_ids, ranker_bounds,
-                      row_chunk=row_chunk)
+    if groups is None:
+        groups = [(b, g) for b in range(B) for g in range(Hkv)]
+    o = np.full((B, L, Hq, D), np.nan)
+    m = np.full((B, Hq, L), np.nan)
+    l = np.full((B, Hq, L), np.nan)
+    for b, g in groups:
+        o_, m_, l_ = forward(q, k, v, p, temperature, segment_ids, ranker_bounds,
+                             heads=range(g * G, (g + 1) * G), batches=[b], row_chunk=row_chunk)
+        hs = slice(g * G, (g + 1) * G)
+        o[b, :, hs], m[b, hs], l[b, hs] = o_[b, :, hs], m_[b, hs], l_[b, hs]
     delta = np.einsum("blhd,blhd->bhl", o, do)
-    dq = np.zeros((B, L, Hq, D))
-    dk = np.zeros((B, L, Hkv, D))
-    dv = np.zeros((B, L, Hkv, D))
+    dq = np.full((B, L, Hq, D), np.nan)
+    dk = np.full((B, L, Hkv, D), np.nan)
+    dv = np.full((B, L, Hkv, D), np.nan)
     rows = np.arange(L)
-    for b in range(B):
-        for hq in range(Hq):
+    for b, g0 in groups:
+        dk[b, :, g0] = 0.0
+        dv[b, :, g0] = 0.0
+        for hq in range(g0 * G, (g0 + 1) * G):
             for rr in _chunks(rows, row_chunk):
                 st = _row_block(q, k, v, b, hq, rr, p, G, temperature, segment_ids,
                                 ranker_bounds)
@@ -302,15 +309,17 @@ def dq_rows(q, k, v, do, p: Params, b, hq, rows, temperature=None, segment_ids=N
 
 
 def dkv_keys(q, k, v, do, p: Params, b, g, keys, temperature=None, segment_ids=None,
-             ranker_bounds=None, row_chunk: int = 512):
+             ranker_bounds=None, row_chunk: int = 512, rows=None):
     """dK, dV for selected keys of one (b, kv head g), summed over the group's
-    query heads.  Needs the full-row statistics of every query row, which are
-    recomputed here by the plain definition."""
+    query heads.  Needs the full-row statistics of every contributing query
+    row, which are recomputed here by the plain definition.  ``rows`` may
+    restrict the sum to the rows that can see the selected keys (a caller's
+    statement about the mask; the omitted rows would add exact zeros)."""
     B, L, Hq, Hkv, D, G = _check(q, k, v)
     keys = np.asarray(keys)
     dk = np.zeros((len(keys), D))
     dv = np.zeros((len(keys), D))
-    rows = np.arange(L)
+    rows = np.arange(L) if rows is None else np.asarray(rows)
     for hq in range(g * G, (g + 1) * G):
         for rr in _chunks(rows, row_chunk):
             st = _row_block(q, k, v, b, hq, rr, p, G, temperature, segment_ids, ranker_bounds)

@@ -1,0 +1,177 @@
+"""CPU tests of the C ABI: the library loads and exports every declared
+symbol, host-side validation rejects bad arguments before any launch, and the
+host planner's pair / tile counts agree with brute force over the oracle's
+visibility predicate."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import blockwise_softmax_attention_amd as ba
+from oracle import Params, visible
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    src = open(os.path.join(ROOT, "include", "attn.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_function():
+    lib = ba.load_library()
+    names = header_functions()
+    assert {"attn_fwd", "attn_bwd_preprocess", "attn_bwd_dq", "attn_bwd_dkv",
+            "attn_plan_count"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert b"gfx950" in lib.attn_build_info()
+
+
+def base_params(**kw):
+    d = dict(batch=1, seq_len=64, q_heads=2, kv_heads=1, head_dim=64, dtype=ba.ATTN_BF16,
+             sm_scale=0.125, causal=True, cap_method=1, cap=30.0)
+    d.update(kw)
+    return ba.AttnParams(**d)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(batch=0), -2), (dict(seq_len=0), -2), (dict(seq_len=300000), -2), (dict(q_heads=0), -2),
+    (dict(dtype=7), -3), (dict(head_dim=96), -4), (dict(q_heads=3, kv_heads=2), -4),
+    (dict(cap_method=9), -6), (dict(window_len=-1), -6), (dict(z_loss_weight=-1.0), -6),
+    (dict(sm_scale=0.0), -6), (dict(sm_scale=float("nan")), -6), (dict(cap=float("inf")), -6),
+])
+def test_params_validation(kw, status):
+    with pytest.raises(ba.AttnError) as e:
+        ba.attn_check_params(base_params(**kw))
+    assert e.value.status == status
+
+
+def test_valid_params_pass():
+    ba.attn_check_params(base_params())
+    ba.attn_check_params(base_params(cap=-1.0, cap_method=3))   # cap <= 0: no cap, still valid
+
+
+def call_raw_fwd(p, ptrs):
+    lib = ba.load_library()
+    cp = p.to_c()
+    return lib.attn_fwd(ctypes.byref(cp), *ptrs, None)
+
+
+def test_null_and_misaligned_pointers_rejected_before_launch():
+    lib = ba.load_library()
+    p = base_params()
+    good = 4096
+    # q, k, v, temp, seg, bounds, o, m, l
+    ptrs = [good, good, good, None, None, None, good, good, good]
+    for idx, name in ((0, "q"), (1, "k"), (2, "v"), (6, "o"), (7, "m"), (8, "l")):
+        bad = list(ptrs)
+        bad[idx] = None
+        assert call_raw_fwd(p, bad) == -1
+        assert name in lib.attn_last_error().decode()
+    bad = list(ptrs)
+    bad[0] = good + 8
+    assert call_raw_fwd(p, bad) == -5
+    bad = list(ptrs)
+    bad[3] = good + 2          # temperature must be 4-byte aligned
+    assert call_raw_fwd(p, bad) == -5
+    # segment ids beyond the segment-table limit
+    p2 = base_params(seq_len=140000)
+    bad = list(ptrs)
+    bad[4] = good
+    assert call_raw_fwd(p2, bad) == -4
+    # backward entry points validate too
+    cp = p.to_c()
+    assert lib.attn_bwd_preprocess(ctypes.byref(cp), None, good, good, None) == -1
+    assert lib.attn_bwd_dq(ctypes.byref(cp), good, good, good, None, None, None, good, good, good,
+                           good, good + 4, None) == -5
+    assert lib.attn_bwd_dkv(ctypes.byref(cp), good, good, good, None, None, None, good, good, good,
+                            good, good, None, None) == -1
+    assert lib.attn_fwd(None, *ptrs, None) == -1
+
+
+def test_status_strings():
+    lib = ba.load_library()
+    for s, n in ba.STATUS_NAMES.items():
+        assert lib.attn_status_str(s).decode() == n
+
+
+# ---------------------------------------------------------------------------
+# Host planner vs brute force
+# ---------------------------------------------------------------------------
+
+BM = 128   # query rows per forward workgroup
+
+
+def brute(L, causal, window, seg, rb, B, bn):
+    p = Params(1.0, causal=causal, window_len=window)
+    pairs = 0
+    tiles_with_pairs = 0
+    for b in range(B):
+        vis = visible(np.arange(L), L, p, None if seg is None else seg[b],
+                      None if rb is None else rb[b])
+        pairs += int(vis.sum())
+        for q0 in range(0, L, BM):
+            for k0 in range(0, L, bn):
+                if vis[q0:q0 + BM, k0:k0 + bn].any():
+                    tiles_with_pairs += 1
+    return pairs, tiles_with_pairs
+
+
+def fwd_bn(dtype, D):
+    return 64 if (dtype == ba.ATTN_BF16 or D == 64) else 32
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_plan_count_matches_brute_force(seed):
+    rng = np.random.default_rng(100 + seed)
+    B = int(rng.integers(1, 3))
+    L = int(rng.integers(1, 700))
+    Hq = int(rng.integers(1, 4))
+    causal = bool(rng.integers(0, 2))
+    window = int(rng.choice([0, 0, 1, 7, 63, 64, 130, 1000]))
+    use_seg = bool(rng.integers(0, 2))
+    use_rk = bool(rng.integers(0, 2))
+    dtype = int(rng.integers(0, 2))
+    D = int(rng.choice([64, 128]))
+    seg = rb = None
+    if use_seg:
+        if rng.integers(0, 2):
+            seg = np.sort(rng.integers(0, 4, size=(B, L)), axis=1).astype(np.int32)   # packed
+        else:
+            seg = rng.integers(0, 3, size=(B, L)).astype(np.int32)                     # arbitrary
+    if use_rk:
+        rb = []
+        for _ in range(B):
+            h = int(rng.integers(0, L + 1))
+            if rng.integers(0, 2):
+                rb.append([0, h, h, L])
+            else:
+                a, b_, c, d = sorted(rng.integers(0, L + 1, size=4))
+                rb.append([a, c, b_, d])        # general (possibly overlapping) bounds
+        rb = np.array(rb, dtype=np.int32)
+    p = ba.AttnParams(batch=B, seq_len=L, q_heads=Hq, kv_heads=1, head_dim=D, dtype=dtype,
+                      sm_scale=1.0, causal=causal, window_len=window)
+    pairs, tiles = ba.attn_plan_count(p, seg, rb)
+    bp, bt = brute(L, causal, window, seg, rb, B, fwd_bn(dtype, D))
+    assert pairs == bp * Hq
+    # sound: every tile holding a visible pair is visited; never more than all tiles
+    n_all = B * ((L + BM - 1) // BM) * ((L + fwd_bn(dtype, D) - 1) // fwd_bn(dtype, D))
+    assert bt * Hq <= tiles <= n_all * Hq
+    if seg is None and not (use_rk and (causal or window)):
+        assert tiles == bt * Hq       # exact for causal/window alone and for the ranker alone
+
+
+def test_plan_count_closed_forms_of_workloads():
+    # causal, L = 32768, 8 heads: 8 L (L + 1) / 2 pairs; W = 512 window on L = 4096
+    p = ba.AttnParams(batch=1, seq_len=32768, q_heads=8, kv_heads=8, head_dim=128, causal=True)
+    assert ba.attn_plan_count(p)[0] == 8 * 32768 * 32769 // 2
+    p = ba.AttnParams(batch=1, seq_len=4096, q_heads=16, kv_heads=16, head_dim=128, causal=True,
+                      window_len=512)
+    assert ba.attn_plan_count(p)[0] == 16 * (512 * 513 // 2 + (4096 - 512) * 512)
+    rb = np.array([[0, 5000, 5000, 8192], [0, 4096, 4096, 8192]], dtype=np.int32)
+    p = ba.AttnParams(batch=2, seq_len=8192, q_heads=16, kv_heads=4, head_dim=128)
+    assert ba.attn_plan_count(p, None, rb)[0] == 16 * sum(8192 * h + 8192 - h for h in (5000, 4096))

@@ -1,0 +1,310 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Bars (float inputs): rel-L2 <= 1e-5 on O, m, l, dQ, dK, dV.
+Bars (bfloat16 inputs): O, dQ, dK, dV rel-L2 <= 8e-3 and max-abs <= 3e-2;
+|dm| <= 1e-3 and |dl| / l <= 1e-3.
+rel-L2 = ||x - ref|| / ||ref|| over the compared entries.
+"""
+import dataclasses
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import blockwise_softmax_attention_amd as ba
+from oracle import Params, backward, dkv_keys, dq_rows
+from workloads import WORKLOADS, Workload, make_inputs, to_f64, to_i32
+
+pytestmark = [pytest.mark.gpu, pytest.mark.filterwarnings("ignore::RuntimeWarning")]
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def oracle_params(w: Workload) -> Params:
+    return Params(w.sm_scale, w.causal, w.window_len, w.cap_method, w.cap, w.alpha, w.beta,
+                  w.z_loss_weight)
+
+
+def host_inputs(inp):
+    return dict(q=to_f64(inp["q"]), k=to_f64(inp["k"]), v=to_f64(inp["v"]), do=to_f64(inp["do"]),
+                temp=to_f64(inp["temperature"]), seg=to_i32(inp["segment_ids"]),
+                rb=to_i32(inp["ranker_bounds"]))
+
+
+def run_gpu(w: Workload, inp, precise=True):
+    p = ba.params_for(w, precise)
+    dev = {k: (v.cuda() if v is not None else None) for k, v in inp.items()}
+    res = ba.attention_forward_backward(p, dev["q"], dev["k"], dev["v"], dev["do"],
+                                        dev["temperature"], dev["segment_ids"], dev["ranker_bounds"])
+    torch.cuda.synchronize()
+    return {k: v.cpu().double().numpy() for k, v in res.items()}
+
+
+def rel_l2(x, ref):
+    n = np.linalg.norm(ref)
+    return np.linalg.norm(x - ref) / (n if n > 0 else 1.0)
+
+
+def check_tensor(name, got, ref, dtype):
+    assert got.shape == ref.shape, name
+    assert np.all(np.isfinite(got)), f"{name}: non-finite values"
+    r = rel_l2(got, ref)
+    ma = float(np.abs(got - ref).max()) if got.size else 0.0
+    say(f"  {name}: rel-L2 {r:.2e} max-abs {ma:.2e}")
+    if dtype == "f32":
+        assert r <= 1e-5, f"{name}: rel-L2 {r:.3e} > 1e-5"
+    else:
+        assert r <= 8e-3, f"{name}: rel-L2 {r:.3e} > 8e-3"
+        assert ma <= 3e-2, f"{name}: max-abs {ma:.3e} > 3e-2"
+
+
+def check_ml(got_m, got_l, ref_m, ref_l, dtype):
+    empty = ~np.isfinite(ref_m)
+    assert np.array_equal(~np.isfinite(got_m), empty), "m: empty rows differ"
+    assert np.all(got_l[empty] == 0) and np.all(ref_l[empty] == 0)
+    gm, rm, gl, rl = got_m[~empty], ref_m[~empty], got_l[~empty], ref_l[~empty]
+    if gm.size == 0:
+        return
+    if dtype == "f32":
+        check_tensor("m", gm, rm, "f32")
+        check_tensor("l", gl, rl, "f32")
+    else:
+        dm = float(np.abs(gm - rm).max())
+        dl = float((np.abs(gl - rl) / rl).max())
+        say(f"  m: max |dm| {dm:.2e}   l: max |dl|/l {dl:.2e}")
+        assert dm <= 1e-3 and dl <= 1e-3
+
+
+def compare_full(w: Workload, precise=True, groups=None):
+    say(f"[parity] {w.name} B{w.B} Hq{w.Hq} Hkv{w.Hkv} L{w.L} D{w.D} {w.dtype} precise={precise}")
+    inp = make_inputs(w)
+    got = run_gpu(w, inp, precise)
+    h = host_inputs(inp)
+    ref = backward(h["q"], h["k"], h["v"], h["do"], oracle_params(w), h["temp"], h["seg"], h["rb"],
+                   groups=groups)
+    G = w.Hq // w.Hkv
+    if groups is None:
+        groups = [(b, g) for b in range(w.B) for g in range(w.Hkv)]
+    for b, g in groups:
+        hs = slice(g * G, (g + 1) * G)
+        check_ml(got["m"][b, hs], got["l"][b, hs], ref["m"][b, hs], ref["l"][b, hs], w.dtype)
+    sel_q = lambda x: np.stack([x[b, :, g * G:(g + 1) * G] for b, g in groups])
+    sel_kv = lambda x: np.stack([x[b, :, g] for b, g in groups])
+    check_tensor("O", sel_q(got["o"]), sel_q(ref["o"]), w.dtype)
+    check_tensor("dQ", sel_q(got["dq"]), sel_q(ref["dq"]), w.dtype)
+    check_tensor("dK", sel_kv(got["dk"]), sel_kv(ref["dk"]), w.dtype)
+    check_tensor("dV", sel_kv(got["dv"]), sel_kv(ref["dv"]), w.dtype)
+    # delta from the fp32 O agrees with the oracle's
+    sel_d = lambda x: np.stack([x[b, g * G:(g + 1) * G] for b, g in groups])
+    check_tensor("delta", sel_d(got["delta"]), sel_d(ref["delta"]), "f32" if w.dtype == "f32" else "bf16")
+    return got
+
+
+# ---------------------------------------------------------------------------
+# The five workloads at reduced sizes (several tiles, ragged tails), every
+# output compared element by element.
+# ---------------------------------------------------------------------------
+REDUCED = {
+    1: WORKLOADS[1],
+    2: WORKLOADS[2].scaled(L=600, Hq=3, Hkv=3),
+    3: WORKLOADS[3].scaled(L=1100, Hq=2, Hkv=2),
+    4: WORKLOADS[4].scaled(L=1000, B=2, Hq=8, Hkv=2),
+    5: WORKLOADS[5].scaled(L=1500, Hq=2, Hkv=2),
+}
+
+
+@pytest.mark.parametrize("cid", [1, 2, 3, 4, 5])
+def test_workload_reduced(cid):
+    compare_full(REDUCED[cid])
+
+
+@pytest.mark.parametrize("cid", [4, 5])
+def test_workload_reduced_single_bf16_ds(cid):
+    compare_full(REDUCED[cid], precise=False)
+
+
+# ---------------------------------------------------------------------------
+# Full sizes.  Workloads 1 and 2 are compared in full; workload 3 on two whole
+# heads; workloads 4 and 5 on sampled rows (O, m, l, dQ), sampled keys (dK,
+# dV) and the column-sum identity sum_j dV_j = sum over visible rows of dO_i.
+# ---------------------------------------------------------------------------
+
+def test_full_workload_2():
+    compare_full(WORKLOADS[2])
+
+
+def test_full_workload_3_two_heads():
+    compare_full(WORKLOADS[3], groups=[(0, 0), (0, 15)])
+
+
+def sampled_checks(w: Workload, rows_by_head, keys, key_rows, b, g):
+    say(f"[parity-sampled] {w.name} b{b} g{g} rows {sum(len(r) for r in rows_by_head.values())} "
+        f"keys {len(keys)}")
+    inp = make_inputs(w)
+    got = run_gpu(w, inp, precise=True)
+    h = host_inputs(inp)
+    p = oracle_params(w)
+    om, ol, oo, odq, gm, gl, go, gdq = [], [], [], [], [], [], [], []
+    for hq, rows in rows_by_head.items():
+        r = dq_rows(h["q"], h["k"], h["v"], h["do"], p, b, hq, rows, h["temp"], h["seg"], h["rb"])
+        om.append(r["m"]); ol.append(r["l"]); oo.append(r["o"]); odq.append(r["dq"])
+        gm.append(got["m"][b, hq, rows]); gl.append(got["l"][b, hq, rows])
+        go.append(got["o"][b, rows, hq]); gdq.append(got["dq"][b, rows, hq])
+    check_ml(np.concatenate(gm), np.concatenate(gl), np.concatenate(om), np.concatenate(ol), w.dtype)
+    check_tensor("O rows", np.concatenate(go), np.concatenate(oo), w.dtype)
+    check_tensor("dQ rows", np.concatenate(gdq), np.concatenate(odq), w.dtype)
+    r = dkv_keys(h["q"], h["k"], h["v"], h["do"], p, b, g, keys, h["temp"], h["seg"], h["rb"],
+                 rows=key_rows)
+    check_tensor("dK keys", got["dk"][b, keys, g], r["dk"], w.dtype)
+    check_tensor("dV keys", got["dv"][b, keys, g], r["dv"], w.dtype)
+    # Every row of these workloads sees at least one key (itself under causality,
+    # itself or the history under the ranker mask), and each row of P sums to 1,
+    # so the sum of dV over all keys of a KV head is the sum of dO over every
+    # row of its query heads.  Tolerance: bf16 rounding of P perturbs each row
+    # sum by ~2^-9 / sqrt(visible keys), far inside 5e-3 of the total.
+    G = w.Hq // w.Hkv
+    for bb in range(w.B):
+        for gg in range(w.Hkv):
+            ref = h["do"][bb, :, gg * G:(gg + 1) * G].sum(axis=(0, 1))
+            tot = got["dv"][bb, :, gg].sum(axis=0)
+            err = np.abs(tot - ref).max() / max(1.0, np.abs(ref).max())
+            say(f"  sum_j dV (b{bb} g{gg}): rel err {err:.2e}")
+            assert err < 5e-3, (bb, gg, err)
+
+
+def test_full_workload_4_sampled():
+    w = WORKLOADS[4]
+    rng = np.random.default_rng(0)
+    b, g = 1, 2
+    rows = np.sort(rng.choice(w.L, 48, replace=False))
+    rows_by_head = {hq: rows for hq in range(g * 4, g * 4 + 4)}
+    keys = np.sort(rng.choice(w.L, 40, replace=False))
+    sampled_checks(w, rows_by_head, keys, None, b, g)
+
+
+def test_full_workload_5_sampled():
+    w = WORKLOADS[5]
+    rng = np.random.default_rng(1)
+    L = w.L
+    rows = np.sort(np.concatenate([rng.choice(L, 40, replace=False), [0, 1, L - 1]]))
+    rows_by_head = {0: rows, 7: rows[::2]}
+    keys = np.sort(rng.choice(np.arange(L - 4096, L), 32, replace=False))
+    # causal: only rows >= the smallest sampled key can see the sampled keys
+    sampled_checks(w, rows_by_head, keys, np.arange(keys.min(), L), 0, 0)
+
+
+# ---------------------------------------------------------------------------
+# Edge cases
+# ---------------------------------------------------------------------------
+
+def W(**kw):
+    base = dict(name="edge", seed=77, B=1, Hq=2, Hkv=1, L=200, D=64, dtype="bf16", sm_scale=0.125,
+                causal=True, window_len=0, cap_method="tanh", cap=30.0)
+    base.update(kw)
+    return Workload(**base)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_length_one(dtype):
+    got = compare_full(W(L=1, dtype=dtype, z_loss_weight=0.1, temperature=(0.5, 1.5)))
+    assert np.allclose(got["l"], 1.0)
+
+
+def test_window_one_returns_v():
+    got = compare_full(W(window_len=1, L=150))
+    inp = make_inputs(W(window_len=1, L=150))
+    v = inp["v"].double().numpy()
+    assert np.allclose(got["o"][0, :, 0], v[0, :, 0], atol=1e-6)
+
+
+def test_fully_masked_rows_and_unseen_keys():
+    # rows 40..59 and 100..199 see nothing; keys 40..59 are seen by nobody
+    w = dataclasses.replace(W(causal=False, L=200, z_loss_weight=0.2), ranker=None)
+    inp = make_inputs(w)
+    inp["ranker_bounds"] = torch.tensor([[0, 40, 60, 100]], dtype=torch.int32)
+    say("[parity] ranker with empty rows")
+    got = run_gpu(w, inp)
+    h = host_inputs(inp)
+    ref = backward(h["q"], h["k"], h["v"], h["do"], oracle_params(w), h["temp"], h["seg"], h["rb"])
+    check_ml(got["m"], got["l"], ref["m"], ref["l"], w.dtype)
+    for n in ("o", "dq", "dk", "dv"):
+        check_tensor(n, got[n], ref[n], w.dtype)
+    assert np.all(got["o"][0, 100:] == 0) and np.all(got["dq"][0, 40:60] == 0)
+    assert np.all(got["dk"][0, 40:60] == 0) and np.all(got["dv"][0, 40:60] == 0)
+
+
+def test_all_rows_empty():
+    w = W(causal=False, L=70)
+    inp = make_inputs(w)
+    inp["ranker_bounds"] = torch.tensor([[5, 5, 9, 9]], dtype=torch.int32)
+    got = run_gpu(w, inp)
+    assert np.all(np.isneginf(got["m"])) and np.all(got["l"] == 0)
+    for n in ("o", "dq", "dk", "dv"):
+        assert np.all(got[n] == 0), n
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_arbitrary_segment_ids(dtype):
+    w = W(dtype=dtype, L=333, Hq=4, Hkv=2, temperature=(0.5, 1.5))
+    inp = make_inputs(w)
+    inp["segment_ids"] = torch.from_numpy(
+        np.random.default_rng(3).integers(0, 3, size=(1, 333)).astype(np.int32))
+    say(f"[parity] arbitrary segment ids {dtype}")
+    got = run_gpu(w, inp)
+    h = host_inputs(inp)
+    ref = backward(h["q"], h["k"], h["v"], h["do"], oracle_params(w), h["temp"], h["seg"], h["rb"])
+    check_ml(got["m"], got["l"], ref["m"], ref["l"], dtype)
+    for n in ("o", "dq", "dk", "dv"):
+        check_tensor(n, got[n], ref[n], dtype)
+
+
+CAPS = [("none", 0.0, 0.0, 0.0), ("tanh", 5.0, 0.0, 0.0), ("soft_sign", 4.0, 0.0, 0.0),
+        ("alsc", 30.0, 4.0, 0.5), ("alsc", 50.0, 2.0, 0.0)]
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("cap", CAPS)
+def test_f32_every_cap(D, cap):
+    m, c, a, b = cap
+    compare_full(W(dtype="f32", D=D, L=290, Hq=4, Hkv=2, cap_method=m, cap=c, alpha=a, beta=b,
+                   z_loss_weight=0.05, temperature=(0.5, 1.5), window_len=150,
+                   sm_scale=1 / math.sqrt(D)))
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("cap", CAPS)
+def test_bf16_every_cap(D, cap):
+    m, c, a, b = cap
+    compare_full(W(dtype="bf16", D=D, L=411, Hq=4, Hkv=1, cap_method=m, cap=c, alpha=a, beta=b,
+                   z_loss_weight=0.01, temperature=(0.8, 1.2), sm_scale=1 / math.sqrt(D)))
+
+
+def test_noncausal_window_literal():
+    compare_full(W(causal=False, window_len=37, L=260, dtype="f32"))
+
+
+def test_gqa_ranker_general_bounds():
+    w = W(causal=True, L=500, Hq=8, Hkv=2, B=2, dtype="f32", cap_method="soft_sign", cap=20.0)
+    inp = make_inputs(w)
+    inp["ranker_bounds"] = torch.tensor([[10, 300, 250, 480], [0, 129, 129, 500]], dtype=torch.int32)
+    say("[parity] gqa ranker with overlapping bounds, causal")
+    got = run_gpu(w, inp)
+    h = host_inputs(inp)
+    ref = backward(h["q"], h["k"], h["v"], h["do"], oracle_params(w), h["temp"], h["seg"], h["rb"])
+    check_ml(got["m"], got["l"], ref["m"], ref["l"], "f32")
+    for n in ("o", "dq", "dk", "dv"):
+        check_tensor(n, got[n], ref[n], "f32")
+
+
+def test_deterministic():
+    w = REDUCED[4]
+    inp = make_inputs(w)
+    a = run_gpu(w, inp)
+    b = run_gpu(w, inp)
+    for n in a:
+        assert np.array_equal(a[n], b[n], equal_nan=True), n
