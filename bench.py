@@ -35,8 +35,11 @@ def parse():
     ap.add_argument("--workload", type=int, default=5, help="workload number 1..5")
     ap.add_argument("--precise-ds", type=int, default=1)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-len", type=int, default=3072,
+    ap.add_argument("--cpu-sample-len", type=int, default=16384,
                     help="prefix length of the oracle's bounded sample")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB (HBM counter "
+                         "calibration) and exit")
     return ap.parse_args()
 
 
@@ -81,6 +84,14 @@ def main():
     from workloads import WORKLOADS, make_inputs
 
     torch.cuda.set_device(0)
+    if args.copy_probe:
+        n = args.copy_probe * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": n * 4}), flush=True)
+        return
     w = WORKLOADS[args.workload]
     inp = make_inputs(w)
     dev = {k: (v.cuda() if v is not None else None) for k, v in inp.items()}

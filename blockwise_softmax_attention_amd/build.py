@@ -20,7 +20,8 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libattn.so")
 ROOT = os.path.dirname(PKG)
 
-SOURCES = ["attn_api.hip", "attn_fwd.hip", "attn_preprocess.hip", "attn_dq.hip", "attn_dkv.hip"]
+SOURCES = ["attn_api.hip", "attn_fwd.hip", "attn_preprocess.hip", "attn_dq.hip", "attn_dkv.hip",
+           "attn_bf16.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

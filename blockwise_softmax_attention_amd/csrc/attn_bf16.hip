@@ -1,0 +1,722 @@
+// bfloat16 kernels for gfx950: forward, dQ and dK/dV.
+//
+// Same mathematics and orientation as the float kernels (see attn_fwd.hip and
+// attn_dq.hip / attn_dkv.hip for the method and its sources), with a
+// gfx950-specific data path:
+//   * K/V (forward, dQ) and Q/dO (dK/dV) tiles are loaded straight from HBM
+//     into LDS (global_load_lds_dwordx4), double-buffered, with no staging
+//     registers;
+//   * each tile is stored once, row-major and swizzled; products that reduce
+//     over the tile rows (P V, dS K, P^T dO, dS^T Q) read it transposed with
+//     ds_read_b64_tr_b16;
+//   * the score elementwise work has a branch-free FULL path for tiles whose
+//     pairs are all visible and a MASKED path for boundary tiles;
+//   * the forward rescales its accumulator only when a row maximum grows by
+//     more than 2^8 (the exact m is tracked separately), so most tiles skip
+//     the rescale.
+#include "attn_bf16.h"
+#include "attn_bwd_common.h"
+
+// Per-kernel build choices (tile size of the dQ kernel; address laundering,
+// see BTile).
+#ifndef ATTN_LAUNDER_FWD
+#define ATTN_LAUNDER_FWD 0
+#endif
+#ifndef ATTN_LAUNDER_DQ
+#define ATTN_LAUNDER_DQ 0
+#endif
+#ifndef ATTN_LAUNDER_DKV
+#define ATTN_LAUNDER_DKV 0
+#endif
+#ifndef ATTN_DQ_BN
+#define ATTN_DQ_BN 32
+#endif
+
+namespace attn {
+
+constexpr int BN16 = 64;     // keys per tile (forward)
+constexpr int BNQ16 = ATTN_DQ_BN;   // keys per tile (dQ: Q and dO fragments stay in registers)
+constexpr int BQ16 = 32;     // queries per tile (dK/dV)
+constexpr float RESCALE_TAU = 8.f;
+
+// Segment-skip table: for the workgroup's own rows [r0, r1), flag the tiles of
+// [t_lo, t_hi) (size bt over the other side) that hold an id inside the
+// workgroup's [min, max] id range.  Sound for any ids.
+__device__ __forceinline__ void segment_flags(const int* segb, int r0, int r1, int t_lo, int t_hi,
+                                              int bt, int L, int tid, unsigned char* flags,
+                                              int* range) {
+  if (tid == 0) {
+    range[0] = 0x7fffffff;
+    range[1] = (int)0x80000000;
+  }
+  __syncthreads();
+  if (tid < r1 - r0) {
+    const int s = segb[r0 + tid];
+    atomicMin(&range[0], s);
+    atomicMax(&range[1], s);
+  }
+  for (int t = t_lo + tid; t < t_hi; t += NTHREADS) flags[t - t_lo] = 0;
+  __syncthreads();
+  const int smin = range[0], smax = range[1];
+  const int end = imin(t_hi * bt, L);
+  for (int x = t_lo * bt + tid; x < end; x += NTHREADS) {
+    const int s = segb[x];
+    if (s >= smin && s <= smax) flags[x / bt - t_lo] = 1;
+  }
+  __syncthreads();
+}
+
+struct RowItem {
+  int b, hkv, hq, q0, q1, qw0, qrow;
+};
+
+__device__ __forceinline__ RowItem decode_row_item(const KArgs& a, int item, int wave, int l32) {
+  RowItem it;
+  const int g = item % a.G;
+  int rest = item / a.G;
+  const int qt_rev = rest % a.n_q_tiles;
+  rest /= a.n_q_tiles;
+  it.hkv = rest % a.Hkv;
+  it.b = rest / a.Hkv;
+  const int qt = a.causal ? (a.n_q_tiles - 1 - qt_rev) : qt_rev;
+  it.hq = it.hkv * a.G + g;
+  it.q0 = qt * BM;
+  it.q1 = imin(it.q0 + BM, a.L);
+  it.qw0 = it.q0 + wave * 32;
+  it.qrow = it.qw0 + l32;
+  return it;
+}
+
+// ---------------------------------------------------------------------------
+// Forward
+// ---------------------------------------------------------------------------
+template <bool MASKED, bool SEG, int CAP, int NKB, int NDB>
+__device__ __forceinline__ void fwd_softmax(f32x16 (&s)[NKB], f32x16 (&o)[NDB], float& m_base,
+                                            float& m_true, float& l_run, const KArgs& a,
+                                            const RowC& rc, const QMask& qm, int k0, int hh,
+                                            const int* sseg, int seg_q) {
+  using CapF = Cap<CAP, false>;
+  float mx = ATTN_NEG_INF;
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float aux;
+      float w = __builtin_fmaf(CapF::f(s[kb][r], a, aux), rc.Kf, rc.C2);
+      if (MASKED) {
+        const int koff = kb * 32 + prow(r, hh);
+        bool vis = qmask_vis(qm, k0 + koff);
+        if (SEG) vis = vis && sseg[koff] == seg_q;
+        w = vis ? w : ATTN_NEG_INF;
+      }
+      s[kb][r] = w;
+      mx = fmaxf(mx, w);
+    }
+  }
+  mx = half_max(mx);
+  m_true = fmaxf(m_true, mx);
+  if (__ballot(mx > m_base + RESCALE_TAU) != 0) {
+    const float m_new = fmaxf(m_base, mx);
+    // 0 when the row saw its first key, 1 while it still has none
+    const float alpha = (m_new == ATTN_NEG_INF) ? 1.f : fast_exp2(m_base - m_new);
+    l_run *= alpha;
+#pragma unroll
+    for (int i = 0; i < NDB; ++i) o[i] *= alpha;
+    m_base = m_new;
+  }
+  const float base = (m_base == ATTN_NEG_INF) ? 0.f : m_base;
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float p = fast_exp2(s[kb][r] - base);
+      l_run += p;
+      s[kb][r] = p;
+    }
+  }
+}
+
+template <int D, int CAP, bool PRECISE>
+__global__ __launch_bounds__(NTHREADS, 2) void fwd_bf16_kernel(KArgs a) {
+  constexpr int BN = BN16;
+  using KT = BTile<BN, D, NWAVES, ATTN_LAUNDER_FWD>;
+  constexpr int NKB = BN / 32, NDB = D / 32, NT16 = D / 16;
+
+  __shared__ __attribute__((aligned(1024))) char sK[2][KT::BYTES];
+  __shared__ __attribute__((aligned(1024))) char sV[2][KT::BYTES];
+  __shared__ int sSeg[2][BN];
+  __shared__ unsigned char sFlag[MAX_TILES];
+  __shared__ int sRange[2];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hh = lane >> 5, l32 = lane & 31;
+  const int item = xcd_remap(blockIdx.x, gridDim.x);
+  if (item >= a.n_items) return;
+  const RowItem it = decode_row_item(a, item, wave, l32);
+  const int L = a.L, b = it.b, qrow = it.qrow;
+  const bool row_ok = qrow < L;
+
+  const long q_rs = (long)a.Hq * D, kv_rs = (long)a.Hkv * D;
+  const bf16* Qb = (const bf16*)a.q + ((long)b * L * a.Hq + it.hq) * D;
+  const bf16* Kb = (const bf16*)a.k + ((long)b * L * a.Hkv + it.hkv) * D;
+  const bf16* Vb = (const bf16*)a.v + ((long)b * L * a.Hkv + it.hkv) * D;
+
+  const MaskSpec ms = load_mask_spec(a, b);
+  const bool has_seg = ms.has_seg;
+  const int* segb = has_seg ? a.seg + (long)b * L : nullptr;
+  const QMask qm = query_mask(qrow, ms);
+
+  bf16x8 qf[NT16];
+#pragma unroll
+  for (int t = 0; t < NT16; ++t) qf[t] = global_frag<bf16>(Qb + (long)qrow * q_rs + 16 * t + 8 * hh, row_ok);
+  const float tmp = (a.temp != nullptr && row_ok) ? a.temp[(long)b * L + qrow] : 1.f;
+  const RowC rc = row_consts(a, tmp, 0.f);
+  const int seg_q = (has_seg && row_ok) ? segb[qrow] : 0;
+
+  int t_lo = 0, t_hi = 0;
+  const bool any = key_tile_range(it.q0, it.q1, BN, ms, &t_lo, &t_hi);
+  if (has_seg && any) segment_flags(segb, it.q0, it.q1, t_lo, t_hi, BN, L, tid, sFlag, sRange);
+  auto next_needed = [&](int t) -> int {
+    for (; t < t_hi; ++t) {
+      if (tile_class(it.q0, it.q1, t * BN, t * BN + BN, ms) == TILE_EMPTY) continue;
+      if (has_seg && !sFlag[t - t_lo]) continue;
+      return t;
+    }
+    return -1;
+  };
+  auto issue = [&](int j, int st) {
+    KT::issue(lds_offset(sK[st]), Kb + (long)(j * BN) * kv_rs, kv_rs, L - j * BN, lane, wave);
+    KT::issue(lds_offset(sV[st]), Vb + (long)(j * BN) * kv_rs, kv_rs, L - j * BN, lane, wave);
+    if (has_seg && tid < BN) sSeg[st][tid] = (j * BN + tid < L) ? segb[j * BN + tid] : -1;
+  };
+
+  float m_base = ATTN_NEG_INF, m_true = ATTN_NEG_INF, l_run = 0.f;
+  f32x16 oacc[NDB];
+#pragma unroll
+  for (int i = 0; i < NDB; ++i) oacc[i] = f32x16{};
+
+  int j = any ? next_needed(t_lo) : -1;
+  if (j >= 0) issue(j, 0);
+  wait_vmcnt<0>();
+  __syncthreads();
+  int st = 0;
+  while (j >= 0) {
+    const int jn = next_needed(j + 1);
+    if (jn >= 0) issue(jn, st ^ 1);
+    const int k0 = j * BN;
+    const char* Kt = sK[st];
+    const char* Vt = sV[st];
+    f32x16 sacc[NKB];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) sacc[kb] = f32x16{};
+#pragma unroll
+    for (int t = 0; t < NT16; ++t) {
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+        sacc[kb] = Elem<bf16>::mfma(KT::row_frag(Kt, kb, t, lane), qf[t], sacc[kb]);
+    }
+    if (tile_class(it.qw0, it.qw0 + 32, k0, k0 + BN, ms) == TILE_FULL) {
+      fwd_softmax<false, false, CAP>(sacc, oacc, m_base, m_true, l_run, a, rc, qm, k0, hh, nullptr, 0);
+    } else if (!has_seg) {
+      fwd_softmax<true, false, CAP>(sacc, oacc, m_base, m_true, l_run, a, rc, qm, k0, hh, nullptr, 0);
+    } else {
+      fwd_softmax<true, true, CAP>(sacc, oacc, m_base, m_true, l_run, a, rc, qm, k0, hh, sSeg[st],
+                                   seg_q);
+    }
+#pragma unroll
+    for (int t = 0; t < BN / 16; ++t) {
+      // With PRECISE, P enters as hi + lo bf16 parts so that O (and the delta
+      // the backward derives from it) carries no bf16 rounding of P.
+      bf16x8 phi, plo;
+      if (PRECISE) {
+        Elem<bf16>::split_acc(sacc[t / 2], 8 * (t % 2), phi, plo);
+      } else {
+        phi = Elem<bf16>::from_acc(sacc[t / 2], 8 * (t % 2));
+      }
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const bf16x8 va = KT::tr_frag(Vt, db, t, lane);
+        oacc[db] = Elem<bf16>::mfma(va, phi, oacc[db]);
+        if (PRECISE) oacc[db] = Elem<bf16>::mfma(va, plo, oacc[db]);
+      }
+    }
+    wait_vmcnt<0>();
+    __syncthreads();
+    st ^= 1;
+    j = jn;
+  }
+
+  const float l_tot = half_sum(l_run);
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  if (row_ok) {
+    float* orow = a.out0 + ((long)(b * L + qrow) * a.Hq + it.hq) * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        f32x4 v;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) v[c] = oacc[db][4 * r4 + c] * inv;
+        *(f32x4*)(orow + 32 * db + 8 * r4 + 4 * hh) = v;
+      }
+    }
+    if (hh == 0) {
+      const long mi = ((long)b * a.Hq + it.hq) * L + qrow;
+      const bool seen = m_true != ATTN_NEG_INF;
+      a.out1[mi] = seen ? m_true * LN2_F : ATTN_NEG_INF;
+      a.out2[mi] = seen ? l_tot * fast_exp2(m_base - m_true) : 0.f;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dQ
+// ---------------------------------------------------------------------------
+template <bool MASKED, bool SEG, int CAP, int NKB>
+__device__ __forceinline__ void dq_elementwise(f32x16 (&s)[NKB], const f32x16 (&dp)[NKB], const KArgs& a,
+                                               const RowC& rc, float dlt, const QMask& qm, int k0,
+                                               int hh, const int* sseg, int seg_q) {
+  using CapF = Cap<CAP, false>;
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float aux;
+      float p = fast_exp2(__builtin_fmaf(CapF::f(s[kb][r], a, aux), rc.Kf, rc.C2));
+      if (MASKED) {
+        const int koff = kb * 32 + prow(r, hh);
+        bool vis = qmask_vis(qm, k0 + koff);
+        if (SEG) vis = vis && sseg[koff] == seg_q;
+        p = vis ? p : 0.f;
+      }
+      s[kb][r] = (p * (dp[kb][r] - dlt)) * (rc.R * CapF::g(aux, a));
+    }
+  }
+}
+
+template <int D, int CAP, bool PRECISE>
+__global__ __launch_bounds__(NTHREADS, 2) void dq_bf16_kernel(KArgs a) {
+  constexpr int BN = BNQ16;
+  using KT = BTile<BN, D, NWAVES, ATTN_LAUNDER_DQ>;
+  constexpr int NKB = BN / 32, NDB = D / 32, NT16 = D / 16;
+
+  __shared__ __attribute__((aligned(1024))) char sK[2][KT::BYTES];
+  __shared__ __attribute__((aligned(1024))) char sV[2][KT::BYTES];
+  __shared__ int sSeg[2][BN];
+  __shared__ unsigned char sFlag[MAX_TILES];
+  __shared__ int sRange[2];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hh = lane >> 5, l32 = lane & 31;
+  const int item = xcd_remap(blockIdx.x, gridDim.x);
+  if (item >= a.n_items) return;
+  const RowItem it = decode_row_item(a, item, wave, l32);
+  const int L = a.L, b = it.b, qrow = it.qrow;
+  const bool row_ok = qrow < L;
+
+  const long q_rs = (long)a.Hq * D, kv_rs = (long)a.Hkv * D;
+  const bf16* Qb = (const bf16*)a.q + ((long)b * L * a.Hq + it.hq) * D;
+  const bf16* dOb = (const bf16*)a.dout + ((long)b * L * a.Hq + it.hq) * D;
+  const bf16* Kb = (const bf16*)a.k + ((long)b * L * a.Hkv + it.hkv) * D;
+  const bf16* Vb = (const bf16*)a.v + ((long)b * L * a.Hkv + it.hkv) * D;
+
+  const MaskSpec ms = load_mask_spec(a, b);
+  const bool has_seg = ms.has_seg;
+  const int* segb = has_seg ? a.seg + (long)b * L : nullptr;
+  const QMask qm = query_mask(qrow, ms);
+
+  bf16x8 qf[NT16], df[NT16];
+#pragma unroll
+  for (int t = 0; t < NT16; ++t) {
+    qf[t] = global_frag<bf16>(Qb + (long)qrow * q_rs + 16 * t + 8 * hh, row_ok);
+    df[t] = global_frag<bf16>(dOb + (long)qrow * q_rs + 16 * t + 8 * hh, row_ok);
+  }
+  float lse2 = ATTN_POS_INF, dlt = 0.f, tmp = 1.f;
+  if (row_ok) {
+    row_residuals(a, ((long)b * a.Hq + it.hq) * L + qrow, lse2, dlt);
+    if (a.temp != nullptr) tmp = a.temp[(long)b * L + qrow];
+  }
+  const RowC rc = row_consts(a, tmp, lse2);
+  const int seg_q = (has_seg && row_ok) ? segb[qrow] : 0;
+
+  int t_lo = 0, t_hi = 0;
+  const bool any = key_tile_range(it.q0, it.q1, BN, ms, &t_lo, &t_hi);
+  if (has_seg && any) segment_flags(segb, it.q0, it.q1, t_lo, t_hi, BN, L, tid, sFlag, sRange);
+  auto next_needed = [&](int t) -> int {
+    for (; t < t_hi; ++t) {
+      if (tile_class(it.q0, it.q1, t * BN, t * BN + BN, ms) == TILE_EMPTY) continue;
+      if (has_seg && !sFlag[t - t_lo]) continue;
+      return t;
+    }
+    return -1;
+  };
+  auto issue = [&](int j, int st) {
+    KT::issue(lds_offset(sK[st]), Kb + (long)(j * BN) * kv_rs, kv_rs, L - j * BN, lane, wave);
+    KT::issue(lds_offset(sV[st]), Vb + (long)(j * BN) * kv_rs, kv_rs, L - j * BN, lane, wave);
+    if (has_seg && tid < BN) sSeg[st][tid] = (j * BN + tid < L) ? segb[j * BN + tid] : -1;
+  };
+
+  f32x16 dqacc[NDB];
+#pragma unroll
+  for (int i = 0; i < NDB; ++i) dqacc[i] = f32x16{};
+
+  int j = any ? next_needed(t_lo) : -1;
+  if (j >= 0) issue(j, 0);
+  wait_vmcnt<0>();
+  __syncthreads();
+  int st = 0;
+  while (j >= 0) {
+    const int jn = next_needed(j + 1);
+    if (jn >= 0) issue(jn, st ^ 1);
+    const int k0 = j * BN;
+    const char* Kt = sK[st];
+    const char* Vt = sV[st];
+    f32x16 sacc[NKB], pacc[NKB];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) sacc[kb] = pacc[kb] = f32x16{};
+#pragma unroll
+    for (int t = 0; t < NT16; ++t) {
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        sacc[kb] = Elem<bf16>::mfma(KT::row_frag(Kt, kb, t, lane), qf[t], sacc[kb]);
+        pacc[kb] = Elem<bf16>::mfma(KT::row_frag(Vt, kb, t, lane), df[t], pacc[kb]);
+      }
+    }
+    if (tile_class(it.qw0, it.qw0 + 32, k0, k0 + BN, ms) == TILE_FULL) {
+      dq_elementwise<false, false, CAP>(sacc, pacc, a, rc, dlt, qm, k0, hh, nullptr, 0);
+    } else if (!has_seg) {
+      dq_elementwise<true, false, CAP>(sacc, pacc, a, rc, dlt, qm, k0, hh, nullptr, 0);
+    } else {
+      dq_elementwise<true, true, CAP>(sacc, pacc, a, rc, dlt, qm, k0, hh, sSeg[st], seg_q);
+    }
+#pragma unroll
+    for (int t = 0; t < BN / 16; ++t) {
+      bf16x8 hi, lo;
+      if (PRECISE) {
+        Elem<bf16>::split_acc(sacc[t / 2], 8 * (t % 2), hi, lo);
+      } else {
+        hi = Elem<bf16>::from_acc(sacc[t / 2], 8 * (t % 2));
+      }
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const bf16x8 ka = KT::tr_frag(Kt, db, t, lane);
+        dqacc[db] = Elem<bf16>::mfma(ka, hi, dqacc[db]);
+        if (PRECISE) dqacc[db] = Elem<bf16>::mfma(ka, lo, dqacc[db]);
+      }
+    }
+    wait_vmcnt<0>();
+    __syncthreads();
+    st ^= 1;
+    j = jn;
+  }
+
+  if (row_ok) {
+    float* drow = a.out0 + ((long)(b * L + qrow) * a.Hq + it.hq) * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        f32x4 v;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) v[c] = dqacc[db][4 * r4 + c];
+        *(f32x4*)(drow + 32 * db + 8 * r4 + 4 * hh) = v;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dK / dV
+// ---------------------------------------------------------------------------
+template <bool MASKED, bool SEG, int CAP, int NQB>
+__device__ __forceinline__ void dkv_elementwise(f32x16 (&s)[NQB], f32x16 (&dp)[NQB], const KArgs& a,
+                                                const float* cKf, const float* cC2, const float* cDl,
+                                                float rratio, const KMask& km, int q0, int hh,
+                                                const int* sseg, int seg_k) {
+  using CapF = Cap<CAP, false>;
+#pragma unroll
+  for (int qb = 0; qb < NQB; ++qb) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int qoff = qb * 32 + prow(r, hh);
+      const float Kf = cKf[qoff], C2 = cC2[qoff], dl = cDl[qoff];
+      float aux;
+      float p = fast_exp2(__builtin_fmaf(CapF::f(s[qb][r], a, aux), Kf, C2));
+      if (MASKED) {
+        bool vis = kmask_vis(km, q0 + qoff);
+        if (SEG) vis = vis && sseg[qoff] == seg_k;
+        p = vis ? p : 0.f;
+      }
+      // R = rmul t = Kf * (rmul / kmul)
+      dp[qb][r] = (p * (dp[qb][r] - dl)) * (Kf * rratio * CapF::g(aux, a));
+      s[qb][r] = p;
+    }
+  }
+}
+
+template <int D, int CAP, bool PRECISE>
+__global__ __launch_bounds__(NTHREADS, 1) void dkv_bf16_kernel(KArgs a) {
+  constexpr int BQ = BQ16;
+  using QT = BTile<BQ, D, NWAVES, ATTN_LAUNDER_DKV>;
+  constexpr int NQB = BQ / 32, NDB = D / 32, NT16 = D / 16;
+
+  __shared__ __attribute__((aligned(1024))) char sQ[2][QT::BYTES];
+  __shared__ __attribute__((aligned(1024))) char sO[2][QT::BYTES];   // dO tile
+  __shared__ __attribute__((aligned(16))) float sKf[2][BQ];
+  __shared__ __attribute__((aligned(16))) float sC2[2][BQ];
+  __shared__ __attribute__((aligned(16))) float sDl[2][BQ];
+  __shared__ int sSeg[2][BQ];
+  __shared__ unsigned char sFlag[MAX_TILES];
+  __shared__ int sRange[2];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hh = lane >> 5, l32 = lane & 31;
+  const int item = xcd_remap(blockIdx.x, gridDim.x);
+  if (item >= a.n_items) return;
+
+  const int L = a.L, G = a.G;
+  const int kt = item % a.n_kv_tiles;
+  const int rest = item / a.n_kv_tiles;
+  const int hkv = rest % a.Hkv;
+  const int b = rest / a.Hkv;
+  const int k0 = kt * BKV, k1 = imin(k0 + BKV, L);
+  const int kw0 = k0 + wave * 32;
+  const int krow = kw0 + l32;
+  const bool key_ok = krow < L;
+
+  const long q_rs = (long)a.Hq * D, kv_rs = (long)a.Hkv * D;
+  const bf16* Kb = (const bf16*)a.k + ((long)b * L * a.Hkv + hkv) * D;
+  const bf16* Vb = (const bf16*)a.v + ((long)b * L * a.Hkv + hkv) * D;
+
+  const MaskSpec ms = load_mask_spec(a, b);
+  const bool has_seg = ms.has_seg;
+  const int* segb = has_seg ? a.seg + (long)b * L : nullptr;
+  const KMask km = key_mask(krow, ms);
+  const float rratio = a.rmul / a.kmul;
+
+  bf16x8 kf[NT16], vf[NT16];
+#pragma unroll
+  for (int t = 0; t < NT16; ++t) {
+    kf[t] = global_frag<bf16>(Kb + (long)krow * kv_rs + 16 * t + 8 * hh, key_ok);
+    vf[t] = global_frag<bf16>(Vb + (long)krow * kv_rs + 16 * t + 8 * hh, key_ok);
+  }
+  const int seg_k = (has_seg && key_ok) ? segb[krow] : 0;
+
+  int t_lo = 0, t_hi = 0;
+  const bool any = query_tile_range(k0, k1, BQ, ms, &t_lo, &t_hi);
+  if (has_seg && any) segment_flags(segb, k0, k1, t_lo, t_hi, BQ, L, tid, sFlag, sRange);
+  auto next_needed = [&](int t) -> int {
+    for (; t < t_hi; ++t) {
+      if (tile_class(t * BQ, t * BQ + BQ, k0, k1, ms) == TILE_EMPTY) continue;
+      if (has_seg && !sFlag[t - t_lo]) continue;
+      return t;
+    }
+    return -1;
+  };
+  auto next_step = [&](int g, int t, int& gn, int& tn) -> bool {
+    int x = next_needed(t + 1);
+    if (x >= 0) {
+      gn = g;
+      tn = x;
+      return true;
+    }
+    if (g + 1 < G) {
+      x = next_needed(t_lo);
+      if (x >= 0) {
+        gn = g + 1;
+        tn = x;
+        return true;
+      }
+    }
+    return false;
+  };
+  // Per-query constants of a step: loaded by the first BQ threads into
+  // registers early, stored to LDS after the current step's compute.
+  float pKf = 0.f, pC2 = 0.f, pDl = 0.f;
+  int pSeg = -1;
+  auto fetch_consts = [&](int g, int t) {
+    if (tid < BQ) {
+      const int hq = hkv * G + g;
+      const int qq = t * BQ + tid;
+      float lse2 = ATTN_POS_INF, dlt = 0.f, tmp = 1.f;
+      pSeg = -1;
+      if (qq < L) {
+        row_residuals(a, ((long)b * a.Hq + hq) * L + qq, lse2, dlt);
+        if (a.temp != nullptr) tmp = a.temp[(long)b * L + qq];
+        if (has_seg) pSeg = segb[qq];
+      }
+      const RowC rc = row_consts(a, tmp, lse2);
+      pKf = rc.Kf;
+      pC2 = rc.C2;
+      pDl = dlt;
+    }
+  };
+  auto store_consts = [&](int stg) {
+    if (tid < BQ) {
+      sKf[stg][tid] = pKf;
+      sC2[stg][tid] = pC2;
+      sDl[stg][tid] = pDl;
+      sSeg[stg][tid] = pSeg;
+    }
+  };
+  auto issue = [&](int g, int t, int stg) {
+    const int hq = hkv * G + g;
+    const int qb0 = t * BQ;
+    QT::issue(lds_offset(sQ[stg]), (const bf16*)a.q + (((long)b * L + qb0) * a.Hq + hq) * D, q_rs,
+              L - qb0, lane, wave);
+    QT::issue(lds_offset(sO[stg]), (const bf16*)a.dout + (((long)b * L + qb0) * a.Hq + hq) * D, q_rs,
+              L - qb0, lane, wave);
+  };
+
+  f32x16 dkacc[NDB], dvacc[NDB];
+#pragma unroll
+  for (int i = 0; i < NDB; ++i) dkacc[i] = dvacc[i] = f32x16{};
+
+  int gc = 0, tc = any ? next_needed(t_lo) : -1;
+  bool have = tc >= 0;
+  if (have) {
+    issue(gc, tc, 0);
+    fetch_consts(gc, tc);
+    store_consts(0);
+  }
+  wait_vmcnt<0>();
+  __syncthreads();
+  int stg = 0;
+  while (have) {
+    int gn = 0, tn = 0;
+    const bool more = next_step(gc, tc, gn, tn);
+    if (more) {
+      issue(gn, tn, stg ^ 1);
+      fetch_consts(gn, tn);
+    }
+    const int q0 = tc * BQ;
+    const char* Qt = sQ[stg];
+    const char* Ot = sO[stg];
+    f32x16 sacc[NQB], pacc[NQB];
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) sacc[qb] = pacc[qb] = f32x16{};
+#pragma unroll
+    for (int t = 0; t < NT16; ++t) {
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb) {
+        sacc[qb] = Elem<bf16>::mfma(QT::row_frag(Qt, qb, t, lane), kf[t], sacc[qb]);
+        pacc[qb] = Elem<bf16>::mfma(QT::row_frag(Ot, qb, t, lane), vf[t], pacc[qb]);
+      }
+    }
+    if (tile_class(q0, q0 + BQ, kw0, kw0 + 32, ms) == TILE_FULL) {
+      dkv_elementwise<false, false, CAP>(sacc, pacc, a, sKf[stg], sC2[stg], sDl[stg], rratio, km, q0,
+                                         hh, nullptr, 0);
+    } else if (!has_seg) {
+      dkv_elementwise<true, false, CAP>(sacc, pacc, a, sKf[stg], sC2[stg], sDl[stg], rratio, km, q0,
+                                        hh, nullptr, 0);
+    } else {
+      dkv_elementwise<true, true, CAP>(sacc, pacc, a, sKf[stg], sC2[stg], sDl[stg], rratio, km, q0,
+                                       hh, sSeg[stg], seg_k);
+    }
+#pragma unroll
+    for (int t = 0; t < BQ / 16; ++t) {
+      const bf16x8 pb = Elem<bf16>::from_acc(sacc[t / 2], 8 * (t % 2));
+      bf16x8 hi, lo;
+      if (PRECISE) {
+        Elem<bf16>::split_acc(pacc[t / 2], 8 * (t % 2), hi, lo);
+      } else {
+        hi = Elem<bf16>::from_acc(pacc[t / 2], 8 * (t % 2));
+      }
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        dvacc[db] = Elem<bf16>::mfma(QT::tr_frag(Ot, db, t, lane), pb, dvacc[db]);
+        const bf16x8 qa = QT::tr_frag(Qt, db, t, lane);
+        dkacc[db] = Elem<bf16>::mfma(qa, hi, dkacc[db]);
+        if (PRECISE) dkacc[db] = Elem<bf16>::mfma(qa, lo, dkacc[db]);
+      }
+    }
+    if (more) store_consts(stg ^ 1);
+    wait_vmcnt<0>();
+    __syncthreads();
+    stg ^= 1;
+    gc = gn;
+    tc = tn;
+    have = more;
+  }
+
+  if (key_ok) {
+    float* dkrow = a.out0 + ((long)(b * L + krow) * a.Hkv + hkv) * D;
+    float* dvrow = a.out1 + ((long)(b * L + krow) * a.Hkv + hkv) * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        f32x4 vk, vv;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          vk[c] = dkacc[db][4 * r4 + c];
+          vv[c] = dvacc[db][4 * r4 + c];
+        }
+        *(f32x4*)(dkrow + 32 * db + 8 * r4 + 4 * hh) = vk;
+        *(f32x4*)(dvrow + 32 * db + 8 * r4 + 4 * hh) = vv;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Launchers
+// ---------------------------------------------------------------------------
+template <int D, bool P>
+static void fwd_bf16_d(const KArgs& a, int cap, hipStream_t s) {
+  dim3 grid(a.n_items), block(NTHREADS);
+  switch (cap) {
+    case 0: hipLaunchKernelGGL((fwd_bf16_kernel<D, 0, P>), grid, block, 0, s, a); break;
+    case 1: hipLaunchKernelGGL((fwd_bf16_kernel<D, 1, P>), grid, block, 0, s, a); break;
+    case 2: hipLaunchKernelGGL((fwd_bf16_kernel<D, 2, P>), grid, block, 0, s, a); break;
+    default: hipLaunchKernelGGL((fwd_bf16_kernel<D, 3, P>), grid, block, 0, s, a); break;
+  }
+}
+
+template <int D, bool P>
+static void dq_bf16_d(const KArgs& a, int cap, hipStream_t s) {
+  dim3 grid(a.n_items), block(NTHREADS);
+  switch (cap) {
+    case 0: hipLaunchKernelGGL((dq_bf16_kernel<D, 0, P>), grid, block, 0, s, a); break;
+    case 1: hipLaunchKernelGGL((dq_bf16_kernel<D, 1, P>), grid, block, 0, s, a); break;
+    case 2: hipLaunchKernelGGL((dq_bf16_kernel<D, 2, P>), grid, block, 0, s, a); break;
+    default: hipLaunchKernelGGL((dq_bf16_kernel<D, 3, P>), grid, block, 0, s, a); break;
+  }
+}
+
+template <int D, bool P>
+static void dkv_bf16_d(const KArgs& a, int cap, hipStream_t s) {
+  dim3 grid(a.n_items), block(NTHREADS);
+  switch (cap) {
+    case 0: hipLaunchKernelGGL((dkv_bf16_kernel<D, 0, P>), grid, block, 0, s, a); break;
+    case 1: hipLaunchKernelGGL((dkv_bf16_kernel<D, 1, P>), grid, block, 0, s, a); break;
+    case 2: hipLaunchKernelGGL((dkv_bf16_kernel<D, 2, P>), grid, block, 0, s, a); break;
+    default: hipLaunchKernelGGL((dkv_bf16_kernel<D, 3, P>), grid, block, 0, s, a); break;
+  }
+}
+
+hipError_t launch_fwd_bf16(const KArgs& a, int head_dim, int cap, hipStream_t s) {
+  const bool p = a.precise_ds != 0;
+  if (head_dim == 64) p ? fwd_bf16_d<64, true>(a, cap, s) : fwd_bf16_d<64, false>(a, cap, s);
+  else p ? fwd_bf16_d<128, true>(a, cap, s) : fwd_bf16_d<128, false>(a, cap, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_dq_bf16(const KArgs& a, int head_dim, int cap, hipStream_t s) {
+  const bool p = a.precise_ds != 0;
+  if (head_dim == 64) p ? dq_bf16_d<64, true>(a, cap, s) : dq_bf16_d<64, false>(a, cap, s);
+  else p ? dq_bf16_d<128, true>(a, cap, s) : dq_bf16_d<128, false>(a, cap, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_dkv_bf16(const KArgs& a, int head_dim, int cap, hipStream_t s) {
+  const bool p = a.precise_ds != 0;
+  if (head_dim == 64) p ? dkv_bf16_d<64, true>(a, cap, s) : dkv_bf16_d<64, false>(a, cap, s);
+  else p ? dkv_bf16_d<128, true>(a, cap, s) : dkv_bf16_d<128, false>(a, cap, s);
+  return hipGetLastError();
+}
+
+}  // namespace attn

@@ -247,14 +247,9 @@ static void dq_cap(const KArgs& a, int cap, hipStream_t s) {
 }
 
 hipError_t launch_dq(const KArgs& a, int dtype, int head_dim, int cap, hipStream_t s) {
-  if (dtype == 1) {
-    const bool p = a.precise_ds != 0;
-    if (head_dim == 64) p ? dq_cap<bf16, 64, true>(a, cap, s) : dq_cap<bf16, 64, false>(a, cap, s);
-    else p ? dq_cap<bf16, 128, true>(a, cap, s) : dq_cap<bf16, 128, false>(a, cap, s);
-  } else {
-    if (head_dim == 64) dq_cap<float, 64, false>(a, cap, s);
-    else dq_cap<float, 128, false>(a, cap, s);
-  }
+  if (dtype == 1) return launch_dq_bf16(a, head_dim, cap, s);
+  if (head_dim == 64) dq_cap<float, 64, false>(a, cap, s);
+  else dq_cap<float, 128, false>(a, cap, s);
   return hipGetLastError();
 }
 

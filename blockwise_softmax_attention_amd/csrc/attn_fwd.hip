@@ -1,4 +1,6 @@
 // Forward kernel: O, m, l of capped, masked, grouped-query softmax attention.
+// This generic version serves float inputs; bfloat16 inputs use the gfx950
+// data path of attn_bf16.hip (same mathematics).
 //
 // Method (triton_kernels.py page, make_triton_forward_kernel; caps from the
 // mosaic_backward.py page, _apply_cap_mosaic): per query row, stream the key
@@ -249,14 +251,12 @@ static hipError_t launch_fwd_t(const KArgs& a, int cap, hipStream_t s) {
 }
 
 hipError_t launch_fwd(const KArgs& a, int dtype, int head_dim, int cap, hipStream_t s) {
-  if (dtype == 1) {
-    return head_dim == 64 ? launch_fwd_t<bf16, 64>(a, cap, s) : launch_fwd_t<bf16, 128>(a, cap, s);
-  }
+  if (dtype == 1) return launch_fwd_bf16(a, head_dim, cap, s);
   return head_dim == 64 ? launch_fwd_t<float, 64>(a, cap, s) : launch_fwd_t<float, 128>(a, cap, s);
 }
 
 int fwd_key_tile(int dtype, int head_dim) {
-  if (dtype == 1) return head_dim == 64 ? FwdCfg<bf16, 64>::BN : FwdCfg<bf16, 128>::BN;
+  if (dtype == 1) return 64;   // attn_bf16.hip
   return head_dim == 64 ? FwdCfg<float, 64>::BN : FwdCfg<float, 128>::BN;
 }
 

@@ -60,5 +60,9 @@ hipError_t launch_preprocess(const KArgs& a, int dtype, int head_dim, hipStream_
 hipError_t launch_dq(const KArgs& a, int dtype, int head_dim, int cap, hipStream_t s);
 hipError_t launch_dkv(const KArgs& a, int dtype, int head_dim, int cap, hipStream_t s);
 int fwd_key_tile(int dtype, int head_dim);   // keys per forward tile
+// bfloat16 kernels (attn_bf16.hip)
+hipError_t launch_fwd_bf16(const KArgs& a, int head_dim, int cap, hipStream_t s);
+hipError_t launch_dq_bf16(const KArgs& a, int head_dim, int cap, hipStream_t s);
+hipError_t launch_dkv_bf16(const KArgs& a, int head_dim, int cap, hipStream_t s);
 
 }  // namespace attn

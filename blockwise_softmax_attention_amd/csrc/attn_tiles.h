@@ -54,10 +54,12 @@ ATTN_HD bool pair_visible(int i, int j, const MaskSpec& s) {
 // exact for each predicate alone and therefore sound for their AND; FULL is
 // only returned when every pair is visible.
 ATTN_HD int tile_class(int q0, int q1, int k0, int k1, const MaskSpec& s) {
+  // FULL means every element of the unclipped block is a visible pair, so a
+  // block reaching past L is at best PARTIAL.
+  bool full = q1 <= s.L && k1 <= s.L;
   q1 = imin(q1, s.L);
   k1 = imin(k1, s.L);
   if (q0 >= q1 || k0 >= k1) return TILE_EMPTY;
-  bool full = true;
   if (s.causal) {
     if (k0 > q1 - 1) return TILE_EMPTY;          // every key after every row
     full = full && (k1 - 1 <= q0);

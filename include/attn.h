@@ -93,8 +93,9 @@ typedef struct {
   int32_t cap_method;   /* attn_cap; a cap <= 0 means no cap whatever the method */
   float cap, alpha, beta;
   float z_loss_weight;  /* w >= 0 */
-  int32_t precise_ds;   /* bf16 only: nonzero rounds dS to a hi+lo pair of bf16
-                           operands for dQ and dK (two MFMAs), zero to one bf16 */
+  int32_t precise_ds;   /* bf16 only: nonzero feeds P (forward P V) and dS (dQ, dK)
+                           to the MFMAs as a hi+lo pair of bf16 operands (two
+                           MFMAs), zero as one bf16 each (faster, less precise) */
 } attn_params;
 
 #define ATTN_MAX_SEQ_LEN 262144

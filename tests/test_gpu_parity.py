@@ -99,9 +99,13 @@ def compare_full(w: Workload, precise=True, groups=None):
     check_tensor("dQ", sel_q(got["dq"]), sel_q(ref["dq"]), w.dtype)
     check_tensor("dK", sel_kv(got["dk"]), sel_kv(ref["dk"]), w.dtype)
     check_tensor("dV", sel_kv(got["dv"]), sel_kv(ref["dv"]), w.dtype)
-    # delta from the fp32 O agrees with the oracle's
+    # delta from the float O agrees with the oracle's; it is a D-term dot
+    # product (magnitude ~ sqrt(D) |O| |dO|), so it is held to the relative bar
+    # of its dtype only.
     sel_d = lambda x: np.stack([x[b, g * G:(g + 1) * G] for b, g in groups])
-    check_tensor("delta", sel_d(got["delta"]), sel_d(ref["delta"]), "f32" if w.dtype == "f32" else "bf16")
+    r = rel_l2(sel_d(got["delta"]), sel_d(ref["delta"]))
+    say(f"  delta: rel-L2 {r:.2e}")
+    assert r <= (1e-5 if w.dtype == "f32" else 8e-3)
     return got
 
 
@@ -142,11 +146,11 @@ def test_full_workload_3_two_heads():
     compare_full(WORKLOADS[3], groups=[(0, 0), (0, 15)])
 
 
-def sampled_checks(w: Workload, rows_by_head, keys, key_rows, b, g):
+def sampled_checks(w: Workload, rows_by_head, keys, key_rows, b, g, precise=True):
     say(f"[parity-sampled] {w.name} b{b} g{g} rows {sum(len(r) for r in rows_by_head.values())} "
-        f"keys {len(keys)}")
+        f"keys {len(keys)} precise={precise}")
     inp = make_inputs(w)
-    got = run_gpu(w, inp, precise=True)
+    got = run_gpu(w, inp, precise=precise)
     h = host_inputs(inp)
     p = oracle_params(w)
     om, ol, oo, odq, gm, gl, go, gdq = [], [], [], [], [], [], [], []
@@ -177,17 +181,19 @@ def sampled_checks(w: Workload, rows_by_head, keys, key_rows, b, g):
             assert err < 5e-3, (bb, gg, err)
 
 
-def test_full_workload_4_sampled():
+@pytest.mark.parametrize("precise", [True, False])
+def test_full_workload_4_sampled(precise):
     w = WORKLOADS[4]
     rng = np.random.default_rng(0)
     b, g = 1, 2
     rows = np.sort(rng.choice(w.L, 48, replace=False))
     rows_by_head = {hq: rows for hq in range(g * 4, g * 4 + 4)}
     keys = np.sort(rng.choice(w.L, 40, replace=False))
-    sampled_checks(w, rows_by_head, keys, None, b, g)
+    sampled_checks(w, rows_by_head, keys, None, b, g, precise)
 
 
-def test_full_workload_5_sampled():
+@pytest.mark.parametrize("precise", [True, False])
+def test_full_workload_5_sampled(precise):
     w = WORKLOADS[5]
     rng = np.random.default_rng(1)
     L = w.L
@@ -195,7 +201,7 @@ def test_full_workload_5_sampled():
     rows_by_head = {0: rows, 7: rows[::2]}
     keys = np.sort(rng.choice(np.arange(L - 4096, L), 32, replace=False))
     # causal: only rows >= the smallest sampled key can see the sampled keys
-    sampled_checks(w, rows_by_head, keys, np.arange(keys.min(), L), 0, 0)
+    sampled_checks(w, rows_by_head, keys, np.arange(keys.min(), L), 0, 0, precise)
 
 
 # ---------------------------------------------------------------------------
@@ -211,8 +217,29 @@ def W(**kw):
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_length_one(dtype):
-    got = compare_full(W(L=1, dtype=dtype, z_loss_weight=0.1, temperature=(0.5, 1.5)))
+    # One key per row: O = V, l = 1, and dS' = P (dP - delta) + w P LSE reduces
+    # to the z-loss term alone because dP = delta exactly.  On the GPU dP (an
+    # MFMA dot product) and delta (the preprocess dot product) are two roundings
+    # of the same O.dO-sized number, so dQ and dK carry an absolute error of a
+    # few float ulps of |dP| times the chain factors, which is large relative
+    # to the small z-loss-only gradient; they are compared against that bound.
+    w = W(L=1, dtype=dtype, z_loss_weight=0.1, temperature=(0.5, 1.5))
+    say(f"[parity] length one {dtype}")
+    inp = make_inputs(w)
+    got = run_gpu(w, inp)
+    h = host_inputs(inp)
+    ref = backward(h["q"], h["k"], h["v"], h["do"], oracle_params(w), h["temp"], h["seg"], h["rb"])
+    check_ml(got["m"], got["l"], ref["m"], ref["l"], dtype)
     assert np.allclose(got["l"], 1.0)
+    for n in ("o", "dv"):
+        check_tensor(n, got[n], ref[n], dtype)
+    dp_scale = np.abs(h["do"]).max() * np.abs(h["v"]).max() * w.D
+    chain = 1.5 * w.sm_scale * max(np.abs(h["k"]).max(), np.abs(h["q"]).max()) * w.Hq
+    bound = 16 * 2.0 ** -24 * dp_scale * chain
+    for n in ("dq", "dk"):
+        err = np.abs(got[n] - ref[n]).max()
+        say(f"  {n}: max-abs {err:.2e} (bound {bound:.2e})")
+        assert err <= bound, (n, err, bound)
 
 
 def test_window_one_returns_v():
