@@ -28,6 +28,9 @@
 #ifndef ATTN_LAUNDER_DKV
 #define ATTN_LAUNDER_DKV 0
 #endif
+#ifndef ATTN_DKV_BQ
+#define ATTN_DKV_BQ 64
+#endif
 #ifndef ATTN_DQ_BN
 #define ATTN_DQ_BN 32
 #endif
@@ -36,7 +39,7 @@ namespace attn {
 
 constexpr int BN16 = 64;     // keys per tile (forward)
 constexpr int BNQ16 = ATTN_DQ_BN;   // keys per tile (dQ: Q and dO fragments stay in registers)
-constexpr int BQ16 = 32;     // queries per tile (dK/dV)
+constexpr int BQ16 = ATTN_DKV_BQ;   // queries per tile (dK/dV)
 constexpr float RESCALE_TAU = 8.f;
 
 // Segment-skip table: for the workgroup's own rows [r0, r1), flag the tiles of
@@ -164,6 +167,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void fwd_bf16_kernel(KArgs a) {
 
   const MaskSpec ms = load_mask_spec(a, b);
   const bool has_seg = ms.has_seg;
+  const bool seg_any = __builtin_amdgcn_readfirstlane((int)has_seg) != 0;
   const int* segb = has_seg ? a.seg + (long)b * L : nullptr;
   const QMask qm = query_mask(qrow, ms);
 
@@ -216,9 +220,12 @@ __global__ __launch_bounds__(NTHREADS, 2) void fwd_bf16_kernel(KArgs a) {
       for (int kb = 0; kb < NKB; ++kb)
         sacc[kb] = Elem<bf16>::mfma(KT::row_frag(Kt, kb, t, lane), qf[t], sacc[kb]);
     }
-    if (tile_class(it.qw0, it.qw0 + 32, k0, k0 + BN, ms) == TILE_FULL) {
+    // the tile class is the same on every lane; readfirstlane lets the compiler
+    // branch on it instead of running every variant under an exec mask
+    const int tcls = __builtin_amdgcn_readfirstlane(tile_class(it.qw0, it.qw0 + 32, k0, k0 + BN, ms));
+    if (tcls == TILE_FULL) {
       fwd_softmax<false, false, CAP>(sacc, oacc, m_base, m_true, l_run, a, rc, qm, k0, hh, nullptr, 0);
-    } else if (!has_seg) {
+    } else if (!seg_any) {
       fwd_softmax<true, false, CAP>(sacc, oacc, m_base, m_true, l_run, a, rc, qm, k0, hh, nullptr, 0);
     } else {
       fwd_softmax<true, true, CAP>(sacc, oacc, m_base, m_true, l_run, a, rc, qm, k0, hh, sSeg[st],
@@ -324,6 +331,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void dq_bf16_kernel(KArgs a) {
 
   const MaskSpec ms = load_mask_spec(a, b);
   const bool has_seg = ms.has_seg;
+  const bool seg_any = __builtin_amdgcn_readfirstlane((int)has_seg) != 0;
   const int* segb = has_seg ? a.seg + (long)b * L : nullptr;
   const QMask qm = query_mask(qrow, ms);
 
@@ -384,9 +392,12 @@ __global__ __launch_bounds__(NTHREADS, 2) void dq_bf16_kernel(KArgs a) {
         pacc[kb] = Elem<bf16>::mfma(KT::row_frag(Vt, kb, t, lane), df[t], pacc[kb]);
       }
     }
-    if (tile_class(it.qw0, it.qw0 + 32, k0, k0 + BN, ms) == TILE_FULL) {
+    // the tile class is the same on every lane; readfirstlane lets the compiler
+    // branch on it instead of running every variant under an exec mask
+    const int tcls = __builtin_amdgcn_readfirstlane(tile_class(it.qw0, it.qw0 + 32, k0, k0 + BN, ms));
+    if (tcls == TILE_FULL) {
       dq_elementwise<false, false, CAP>(sacc, pacc, a, rc, dlt, qm, k0, hh, nullptr, 0);
-    } else if (!has_seg) {
+    } else if (!seg_any) {
       dq_elementwise<true, false, CAP>(sacc, pacc, a, rc, dlt, qm, k0, hh, nullptr, 0);
     } else {
       dq_elementwise<true, true, CAP>(sacc, pacc, a, rc, dlt, qm, k0, hh, sSeg[st], seg_q);
@@ -493,6 +504,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void dkv_bf16_kernel(KArgs a) {
 
   const MaskSpec ms = load_mask_spec(a, b);
   const bool has_seg = ms.has_seg;
+  const bool seg_any = __builtin_amdgcn_readfirstlane((int)has_seg) != 0;
   const int* segb = has_seg ? a.seg + (long)b * L : nullptr;
   const KMask km = key_mask(krow, ms);
   const float rratio = a.rmul / a.kmul;
@@ -606,10 +618,13 @@ __global__ __launch_bounds__(NTHREADS, 1) void dkv_bf16_kernel(KArgs a) {
         pacc[qb] = Elem<bf16>::mfma(QT::row_frag(Ot, qb, t, lane), vf[t], pacc[qb]);
       }
     }
-    if (tile_class(q0, q0 + BQ, kw0, kw0 + 32, ms) == TILE_FULL) {
+    // the tile class is the same on every lane; readfirstlane lets the compiler
+    // branch on it instead of running every variant under an exec mask
+    const int tcls = __builtin_amdgcn_readfirstlane(tile_class(q0, q0 + BQ, kw0, kw0 + 32, ms));
+    if (tcls == TILE_FULL) {
       dkv_elementwise<false, false, CAP>(sacc, pacc, a, sKf[stg], sC2[stg], sDl[stg], rratio, km, q0,
                                          hh, nullptr, 0);
-    } else if (!has_seg) {
+    } else if (!seg_any) {
       dkv_elementwise<true, false, CAP>(sacc, pacc, a, sKf[stg], sC2[stg], sDl[stg], rratio, km, q0,
                                         hh, nullptr, 0);
     } else {
