@@ -114,6 +114,22 @@ struct BTile {
     }
   }
 
+  // Load i (0 <= i < PER_WAVE) of this wave's share of one tile, the same
+  // instruction issue() would send; lets a kernel spread its loads over its
+  // compute instead of sending them in one burst.
+  __device__ __forceinline__ static void issue_one(uint32_t lds_base, const bf16* gbase, long row_stride,
+                                                   int rows_valid, int lane, int wave, int i) {
+    constexpr int LPR = RB / 16;
+    constexpr int RPI = 64 / LPR;
+    const int x = wave * RPI + lane / LPR;
+    const int pos = lane % LPR;
+    const int c = pos ^ swz(x);
+    const int n = wave + NW * i;
+    const int prow = imin(i * RPI * NW + pi32(x), rows_valid - 1);
+    dma16(gbase + (long)prow * row_stride + c * 8,
+          (uint32_t)__builtin_amdgcn_readfirstlane(lds_base + n * 1024));
+  }
+
   // A operand, reduction over D: rows blk*32 + lane%32 (LDS order), step t.
   __device__ __forceinline__ static bf16x8 row_frag(const char* lds, int blk, int t, int lane) {
     if (LAUNDER) asm volatile("" : "+v"(lane));

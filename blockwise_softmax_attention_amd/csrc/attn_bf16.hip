@@ -28,6 +28,12 @@
 #ifndef ATTN_LAUNDER_DKV
 #define ATTN_LAUNDER_DKV 0
 #endif
+#ifndef ATTN_FWD_BN
+#define ATTN_FWD_BN 64
+#endif
+#ifndef ATTN_FWD_WAVES_PER_SIMD
+#define ATTN_FWD_WAVES_PER_SIMD 2
+#endif
 #ifndef ATTN_DKV_BQ
 #define ATTN_DKV_BQ 64
 #endif
@@ -37,7 +43,7 @@
 
 namespace attn {
 
-constexpr int BN16 = 64;     // keys per tile (forward)
+constexpr int BN16 = ATTN_FWD_BN;   // keys per tile (forward)
 constexpr int BNQ16 = ATTN_DQ_BN;   // keys per tile (dQ: Q and dO fragments stay in registers)
 constexpr int BQ16 = ATTN_DKV_BQ;   // queries per tile (dK/dV)
 constexpr float RESCALE_TAU = 8.f;
@@ -140,7 +146,7 @@ __device__ __forceinline__ void fwd_softmax(f32x16 (&s)[NKB], f32x16 (&o)[NDB], 
 }
 
 template <int D, int CAP, bool PRECISE>
-__global__ __launch_bounds__(NTHREADS, 2) void fwd_bf16_kernel(KArgs a) {
+__global__ __launch_bounds__(NTHREADS, ATTN_FWD_WAVES_PER_SIMD) void fwd_bf16_kernel(KArgs a) {
   constexpr int BN = BN16;
   using KT = BTile<BN, D, NWAVES, ATTN_LAUNDER_FWD>;
   constexpr int NKB = BN / 32, NDB = D / 32, NT16 = D / 16;
@@ -189,10 +195,27 @@ __global__ __launch_bounds__(NTHREADS, 2) void fwd_bf16_kernel(KArgs a) {
     }
     return -1;
   };
+  int pseg = -1;
   auto issue = [&](int j, int st) {
     KT::issue(lds_offset(sK[st]), Kb + (long)(j * BN) * kv_rs, kv_rs, L - j * BN, lane, wave);
     KT::issue(lds_offset(sV[st]), Vb + (long)(j * BN) * kv_rs, kv_rs, L - j * BN, lane, wave);
-    if (has_seg && tid < BN) sSeg[st][tid] = (j * BN + tid < L) ? segb[j * BN + tid] : -1;
+  };
+  // load i of this wave's 2 PER_WAVE loads of the K and V tiles of key tile j
+  auto issue_one = [&](int j, int st, int i) {
+    if (i < KT::PER_WAVE)
+      KT::issue_one(lds_offset(sK[st]), Kb + (long)(j * BN) * kv_rs, kv_rs, L - j * BN, lane, wave, i);
+    else
+      KT::issue_one(lds_offset(sV[st]), Vb + (long)(j * BN) * kv_rs, kv_rs, L - j * BN, lane, wave,
+                    i - KT::PER_WAVE);
+  };
+  constexpr int NDMA = 2 * KT::PER_WAVE;
+  auto load_seg = [&](int j) {
+    if (has_seg && tid < BN) pseg = (j * BN + tid < L) ? segb[j * BN + tid] : -1;
+  };
+  // the key segment ids go to LDS at the end of the step, after their load's
+  // latency has passed
+  auto store_seg = [&](int st) {
+    if (has_seg && tid < BN) sSeg[st][tid] = pseg;
   };
 
   float m_base = ATTN_NEG_INF, m_true = ATTN_NEG_INF, l_run = 0.f;
@@ -201,25 +224,48 @@ __global__ __launch_bounds__(NTHREADS, 2) void fwd_bf16_kernel(KArgs a) {
   for (int i = 0; i < NDB; ++i) oacc[i] = f32x16{};
 
   int j = any ? next_needed(t_lo) : -1;
-  if (j >= 0) issue(j, 0);
+  if (j >= 0) {
+    issue(j, 0);
+    load_seg(j);
+    store_seg(0);
+  }
   wait_vmcnt<0>();
   __syncthreads();
   int st = 0;
   while (j >= 0) {
     const int jn = next_needed(j + 1);
-    if (jn >= 0) issue(jn, st ^ 1);
+    // tile loaded during this step: the next one, or (without one) the
+    // current tile again into the idle stage, which keeps the body branch-free
+    const int jl = jn >= 0 ? jn : j;
     const int k0 = j * BN;
     const char* Kt = sK[st];
     const char* Vt = sV[st];
     f32x16 sacc[NKB];
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) sacc[kb] = f32x16{};
+    // LDS fragments of step t + 1 requested before the MFMAs of step t (see
+    // the dK/dV kernel)
+    bf16x8 fk[2][NKB];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) fk[0][kb] = KT::row_frag(Kt, kb, 0, lane);
 #pragma unroll
     for (int t = 0; t < NT16; ++t) {
+      const int cur = t & 1;
+      if (t + 1 < NT16) {
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-        sacc[kb] = Elem<bf16>::mfma(KT::row_frag(Kt, kb, t, lane), qf[t], sacc[kb]);
+        for (int kb = 0; kb < NKB; ++kb) fk[cur ^ 1][kb] = KT::row_frag(Kt, kb, t + 1, lane);
+      }
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) sacc[kb] = Elem<bf16>::mfma(fk[cur][kb], qf[t], sacc[kb]);
+      if (t + 1 < NT16) __builtin_amdgcn_sched_group_barrier(0x100, NKB, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, NKB, 0);
+      // the next tile's loads, spread over the reduction steps: sent in one
+      // burst they keep the wave waiting at issue
+#pragma unroll
+      for (int i = t * NDMA / NT16; i < (t + 1) * NDMA / NT16; ++i) issue_one(jl, st ^ 1, i);
+      __builtin_amdgcn_sched_barrier(0);
     }
+    load_seg(jl);
     // the tile class is the same on every lane; readfirstlane lets the compiler
     // branch on it instead of running every variant under an exec mask
     const int tcls = __builtin_amdgcn_readfirstlane(tile_class(it.qw0, it.qw0 + 32, k0, k0 + BN, ms));
@@ -248,6 +294,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void fwd_bf16_kernel(KArgs a) {
         if (PRECISE) oacc[db] = Elem<bf16>::mfma(va, plo, oacc[db]);
       }
     }
+    if (jn >= 0) store_seg(st ^ 1);
     wait_vmcnt<0>();
     __syncthreads();
     st ^= 1;
@@ -360,10 +407,27 @@ __global__ __launch_bounds__(NTHREADS, 2) void dq_bf16_kernel(KArgs a) {
     }
     return -1;
   };
+  int pseg = -1;
   auto issue = [&](int j, int st) {
     KT::issue(lds_offset(sK[st]), Kb + (long)(j * BN) * kv_rs, kv_rs, L - j * BN, lane, wave);
     KT::issue(lds_offset(sV[st]), Vb + (long)(j * BN) * kv_rs, kv_rs, L - j * BN, lane, wave);
-    if (has_seg && tid < BN) sSeg[st][tid] = (j * BN + tid < L) ? segb[j * BN + tid] : -1;
+  };
+  // load i of this wave's 2 PER_WAVE loads of the K and V tiles of key tile j
+  auto issue_one = [&](int j, int st, int i) {
+    if (i < KT::PER_WAVE)
+      KT::issue_one(lds_offset(sK[st]), Kb + (long)(j * BN) * kv_rs, kv_rs, L - j * BN, lane, wave, i);
+    else
+      KT::issue_one(lds_offset(sV[st]), Vb + (long)(j * BN) * kv_rs, kv_rs, L - j * BN, lane, wave,
+                    i - KT::PER_WAVE);
+  };
+  constexpr int NDMA = 2 * KT::PER_WAVE;
+  auto load_seg = [&](int j) {
+    if (has_seg && tid < BN) pseg = (j * BN + tid < L) ? segb[j * BN + tid] : -1;
+  };
+  // the key segment ids go to LDS at the end of the step, after their load's
+  // latency has passed
+  auto store_seg = [&](int st) {
+    if (has_seg && tid < BN) sSeg[st][tid] = pseg;
   };
 
   f32x16 dqacc[NDB];
@@ -371,27 +435,56 @@ __global__ __launch_bounds__(NTHREADS, 2) void dq_bf16_kernel(KArgs a) {
   for (int i = 0; i < NDB; ++i) dqacc[i] = f32x16{};
 
   int j = any ? next_needed(t_lo) : -1;
-  if (j >= 0) issue(j, 0);
+  if (j >= 0) {
+    issue(j, 0);
+    load_seg(j);
+    store_seg(0);
+  }
   wait_vmcnt<0>();
   __syncthreads();
   int st = 0;
   while (j >= 0) {
     const int jn = next_needed(j + 1);
-    if (jn >= 0) issue(jn, st ^ 1);
+    // tile loaded during this step: the next one, or (without one) the
+    // current tile again into the idle stage, which keeps the body branch-free
+    const int jl = jn >= 0 ? jn : j;
     const int k0 = j * BN;
     const char* Kt = sK[st];
     const char* Vt = sV[st];
     f32x16 sacc[NKB], pacc[NKB];
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) sacc[kb] = pacc[kb] = f32x16{};
+    // LDS fragments of reduction step t + 1 requested before the MFMAs of
+    // step t; the fences keep the compiler from sinking them next to their use
+    bf16x8 fk[2][NKB], fv[2][NKB];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      fk[0][kb] = KT::row_frag(Kt, kb, 0, lane);
+      fv[0][kb] = KT::row_frag(Vt, kb, 0, lane);
+    }
 #pragma unroll
     for (int t = 0; t < NT16; ++t) {
+      const int cur = t & 1;
+      if (t + 1 < NT16) {
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+          fk[cur ^ 1][kb] = KT::row_frag(Kt, kb, t + 1, lane);
+          fv[cur ^ 1][kb] = KT::row_frag(Vt, kb, t + 1, lane);
+        }
+      }
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
-        sacc[kb] = Elem<bf16>::mfma(KT::row_frag(Kt, kb, t, lane), qf[t], sacc[kb]);
-        pacc[kb] = Elem<bf16>::mfma(KT::row_frag(Vt, kb, t, lane), df[t], pacc[kb]);
+        sacc[kb] = Elem<bf16>::mfma(fk[cur][kb], qf[t], sacc[kb]);
+        pacc[kb] = Elem<bf16>::mfma(fv[cur][kb], df[t], pacc[kb]);
       }
+      if (t + 1 < NT16) __builtin_amdgcn_sched_group_barrier(0x100, 2 * NKB, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 2 * NKB, 0);
+      // the next tile's loads, spread over the reduction steps
+#pragma unroll
+      for (int i = t * NDMA / NT16; i < (t + 1) * NDMA / NT16; ++i) issue_one(jl, st ^ 1, i);
+      __builtin_amdgcn_sched_barrier(0);
     }
+    load_seg(jl);
     // the tile class is the same on every lane; readfirstlane lets the compiler
     // branch on it instead of running every variant under an exec mask
     const int tcls = __builtin_amdgcn_readfirstlane(tile_class(it.qw0, it.qw0 + 32, k0, k0 + BN, ms));
@@ -417,6 +510,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void dq_bf16_kernel(KArgs a) {
         if (PRECISE) dqacc[db] = Elem<bf16>::mfma(ka, lo, dqacc[db]);
       }
     }
+    if (jn >= 0) store_seg(st ^ 1);
     wait_vmcnt<0>();
     __syncthreads();
     st ^= 1;
@@ -444,7 +538,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void dq_bf16_kernel(KArgs a) {
 template <bool MASKED, bool SEG, int CAP, int NQB>
 __device__ __forceinline__ void dkv_elementwise(f32x16 (&s)[NQB], f32x16 (&dp)[NQB], const KArgs& a,
                                                 const float* cKf, const float* cC2, const float* cDl,
-                                                float rratio, const KMask& km, int q0, int hh,
+                                                const float* cR, const KMask& km, int q0, int hh,
                                                 const int* sseg, int seg_k) {
   using CapF = Cap<CAP, false>;
 #pragma unroll
@@ -452,7 +546,7 @@ __device__ __forceinline__ void dkv_elementwise(f32x16 (&s)[NQB], f32x16 (&dp)[N
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int qoff = qb * 32 + prow(r, hh);
-      const float Kf = cKf[qoff], C2 = cC2[qoff], dl = cDl[qoff];
+      const float Kf = cKf[qoff], C2 = cC2[qoff], dl = cDl[qoff], R = cR[qoff];
       float aux;
       float p = fast_exp2(__builtin_fmaf(CapF::f(s[qb][r], a, aux), Kf, C2));
       if (MASKED) {
@@ -460,8 +554,7 @@ __device__ __forceinline__ void dkv_elementwise(f32x16 (&s)[NQB], f32x16 (&dp)[N
         if (SEG) vis = vis && sseg[qoff] == seg_k;
         p = vis ? p : 0.f;
       }
-      // R = rmul t = Kf * (rmul / kmul)
-      dp[qb][r] = (p * (dp[qb][r] - dl)) * (Kf * rratio * CapF::g(aux, a));
+      dp[qb][r] = (p * (dp[qb][r] - dl)) * (R * CapF::g(aux, a));
       s[qb][r] = p;
     }
   }
@@ -478,6 +571,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void dkv_bf16_kernel(KArgs a) {
   __shared__ __attribute__((aligned(16))) float sKf[2][BQ];
   __shared__ __attribute__((aligned(16))) float sC2[2][BQ];
   __shared__ __attribute__((aligned(16))) float sDl[2][BQ];
+  __shared__ __attribute__((aligned(16))) float sR[2][BQ];
   __shared__ int sSeg[2][BQ];
   __shared__ unsigned char sFlag[MAX_TILES];
   __shared__ int sRange[2];
@@ -507,7 +601,6 @@ __global__ __launch_bounds__(NTHREADS, 1) void dkv_bf16_kernel(KArgs a) {
   const bool seg_any = __builtin_amdgcn_readfirstlane((int)has_seg) != 0;
   const int* segb = has_seg ? a.seg + (long)b * L : nullptr;
   const KMask km = key_mask(krow, ms);
-  const float rratio = a.rmul / a.kmul;
 
   bf16x8 kf[NT16], vf[NT16];
 #pragma unroll
@@ -545,33 +638,43 @@ __global__ __launch_bounds__(NTHREADS, 1) void dkv_bf16_kernel(KArgs a) {
     }
     return false;
   };
-  // Per-query constants of a step: loaded by the first BQ threads into
-  // registers early, stored to LDS after the current step's compute.
-  float pKf = 0.f, pC2 = 0.f, pDl = 0.f;
+  // Per-query inputs of the next step (m, l, delta, temperature, segment id):
+  // each wave loads BQ / NWAVES of them into registers when the step's tile
+  // loads are issued, and derives the constants from them only after the
+  // current step's compute, so that their latency hides behind it.
+  constexpr int CPW = BQ / NWAVES;
+  static_assert(CPW <= 64 && BQ % NWAVES == 0, "constant fetch layout");
+  const int cq = wave * CPW + lane;
+  const bool cthr = lane < CPW;
+  float pM = 0.f, pL = 0.f, pD = 0.f, pT = 1.f;
   int pSeg = -1;
   auto fetch_consts = [&](int g, int t) {
-    if (tid < BQ) {
+    if (cthr) {
       const int hq = hkv * G + g;
-      const int qq = t * BQ + tid;
-      float lse2 = ATTN_POS_INF, dlt = 0.f, tmp = 1.f;
+      const int qq = t * BQ + cq;
+      pL = 0.f;
+      pT = 1.f;
       pSeg = -1;
       if (qq < L) {
-        row_residuals(a, ((long)b * a.Hq + hq) * L + qq, lse2, dlt);
-        if (a.temp != nullptr) tmp = a.temp[(long)b * L + qq];
+        const long idx = ((long)b * a.Hq + hq) * L + qq;
+        pM = a.m_in[idx];
+        pL = a.l_in[idx];
+        pD = a.delta_in[idx];
+        if (a.temp != nullptr) pT = a.temp[(long)b * L + qq];
         if (has_seg) pSeg = segb[qq];
       }
-      const RowC rc = row_consts(a, tmp, lse2);
-      pKf = rc.Kf;
-      pC2 = rc.C2;
-      pDl = dlt;
     }
   };
   auto store_consts = [&](int stg) {
-    if (tid < BQ) {
-      sKf[stg][tid] = pKf;
-      sC2[stg][tid] = pC2;
-      sDl[stg][tid] = pDl;
-      sSeg[stg][tid] = pSeg;
+    if (cthr) {
+      float lse2, dlt;
+      residuals_from(pM, pL, pD, a.zw, lse2, dlt);
+      const RowC rc = row_consts(a, pT, lse2);
+      sKf[stg][cq] = rc.Kf;
+      sC2[stg][cq] = rc.C2;
+      sDl[stg][cq] = dlt;
+      sR[stg][cq] = rc.R;
+      sSeg[stg][cq] = pSeg;
     }
   };
   auto issue = [&](int g, int t, int stg) {
@@ -582,6 +685,20 @@ __global__ __launch_bounds__(NTHREADS, 1) void dkv_bf16_kernel(KArgs a) {
     QT::issue(lds_offset(sO[stg]), (const bf16*)a.dout + (((long)b * L + qb0) * a.Hq + hq) * D, q_rs,
               L - qb0, lane, wave);
   };
+  // Load i of the 2 PER_WAVE loads of this wave for the Q and dO tiles of
+  // step (g, t): the first PER_WAVE go to Q, the rest to dO.
+  auto issue_one = [&](int g, int t, int stg, int i) {
+    const int hq = hkv * G + g;
+    const int qb0 = t * BQ;
+    if (i < QT::PER_WAVE) {
+      QT::issue_one(lds_offset(sQ[stg]), (const bf16*)a.q + (((long)b * L + qb0) * a.Hq + hq) * D, q_rs,
+                    L - qb0, lane, wave, i);
+    } else {
+      QT::issue_one(lds_offset(sO[stg]), (const bf16*)a.dout + (((long)b * L + qb0) * a.Hq + hq) * D, q_rs,
+                    L - qb0, lane, wave, i - QT::PER_WAVE);
+    }
+  };
+  constexpr int NDMA = 2 * QT::PER_WAVE;
 
   f32x16 dkacc[NDB], dvacc[NDB];
 #pragma unroll
@@ -598,11 +715,13 @@ __global__ __launch_bounds__(NTHREADS, 1) void dkv_bf16_kernel(KArgs a) {
   __syncthreads();
   int stg = 0;
   while (have) {
-    int gn = 0, tn = 0;
+    int gn = gc, tn = tc;
+    // without a next step, the loads below refetch the current tile into the
+    // idle stage (branch-free loop body; once per work-group)
     const bool more = next_step(gc, tc, gn, tn);
-    if (more) {
-      issue(gn, tn, stg ^ 1);
-      fetch_consts(gn, tn);
+    if (!more) {
+      gn = gc;
+      tn = tc;
     }
     const int q0 = tc * BQ;
     const char* Qt = sQ[stg];
@@ -610,25 +729,51 @@ __global__ __launch_bounds__(NTHREADS, 1) void dkv_bf16_kernel(KArgs a) {
     f32x16 sacc[NQB], pacc[NQB];
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb) sacc[qb] = pacc[qb] = f32x16{};
+    // Software pipeline over the reduction steps: the LDS fragments of step
+    // t + 1 are requested before the MFMAs of step t, and a scheduling fence
+    // keeps the compiler from sinking them next to their use (which would
+    // expose one LDS latency per MFMA).
+    bf16x8 fq[2][NQB], fo[2][NQB];
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) {
+      fq[0][qb] = QT::row_frag(Qt, qb, 0, lane);
+      fo[0][qb] = QT::row_frag(Ot, qb, 0, lane);
+    }
 #pragma unroll
     for (int t = 0; t < NT16; ++t) {
+      const int cur = t & 1;
+      if (t + 1 < NT16) {
+#pragma unroll
+        for (int qb = 0; qb < NQB; ++qb) {
+          fq[cur ^ 1][qb] = QT::row_frag(Qt, qb, t + 1, lane);
+          fo[cur ^ 1][qb] = QT::row_frag(Ot, qb, t + 1, lane);
+        }
+      }
 #pragma unroll
       for (int qb = 0; qb < NQB; ++qb) {
-        sacc[qb] = Elem<bf16>::mfma(QT::row_frag(Qt, qb, t, lane), kf[t], sacc[qb]);
-        pacc[qb] = Elem<bf16>::mfma(QT::row_frag(Ot, qb, t, lane), vf[t], pacc[qb]);
+        sacc[qb] = Elem<bf16>::mfma(fq[cur][qb], kf[t], sacc[qb]);
+        pacc[qb] = Elem<bf16>::mfma(fo[cur][qb], vf[t], pacc[qb]);
       }
+      if (t + 1 < NT16) __builtin_amdgcn_sched_group_barrier(0x100, 2 * NQB, 0);   // LDS reads
+      __builtin_amdgcn_sched_group_barrier(0x008, 2 * NQB, 0);                      // then MFMAs
+      // the next step's tile loads, spread over the reduction steps: sent in
+      // one burst they keep the wave waiting at issue
+#pragma unroll
+      for (int i = t * NDMA / NT16; i < (t + 1) * NDMA / NT16; ++i) issue_one(gn, tn, stg ^ 1, i);
+      __builtin_amdgcn_sched_barrier(0);
     }
+    fetch_consts(gn, tn);
     // the tile class is the same on every lane; readfirstlane lets the compiler
     // branch on it instead of running every variant under an exec mask
     const int tcls = __builtin_amdgcn_readfirstlane(tile_class(q0, q0 + BQ, kw0, kw0 + 32, ms));
     if (tcls == TILE_FULL) {
-      dkv_elementwise<false, false, CAP>(sacc, pacc, a, sKf[stg], sC2[stg], sDl[stg], rratio, km, q0,
+      dkv_elementwise<false, false, CAP>(sacc, pacc, a, sKf[stg], sC2[stg], sDl[stg], sR[stg], km, q0,
                                          hh, nullptr, 0);
     } else if (!seg_any) {
-      dkv_elementwise<true, false, CAP>(sacc, pacc, a, sKf[stg], sC2[stg], sDl[stg], rratio, km, q0,
+      dkv_elementwise<true, false, CAP>(sacc, pacc, a, sKf[stg], sC2[stg], sDl[stg], sR[stg], km, q0,
                                         hh, nullptr, 0);
     } else {
-      dkv_elementwise<true, true, CAP>(sacc, pacc, a, sKf[stg], sC2[stg], sDl[stg], rratio, km, q0,
+      dkv_elementwise<true, true, CAP>(sacc, pacc, a, sKf[stg], sC2[stg], sDl[stg], sR[stg], km, q0,
                                        hh, sSeg[stg], seg_k);
     }
 #pragma unroll

@@ -166,8 +166,8 @@ template <> struct Cap<1, false> {         // tanh(y) = 1 - 2 / (e^{2y} + 1)
     aux = r;
     return r;
   }
-  // 1 - tanh^2 = 4 r (1 - r); the 4 is in rmul
-  __device__ __forceinline__ static float g(float r, const KArgs&) { return r * (1.f - r); }
+  // 1 - tanh^2 = 4 r (1 - r); the 4 is in rmul.  r - r^2 in one fma (single rounding).
+  __device__ __forceinline__ static float g(float r, const KArgs&) { return __builtin_fmaf(-r, r, r); }
 };
 
 template <> struct Cap<1, true> {
@@ -203,8 +203,8 @@ template <> struct Cap<3, false> {         // cap (sig(z) - sig(ab)) / denom
     aux = r;
     return r;
   }
-  // sig(z)(1 - sig(z)); alpha / denom is in rmul
-  __device__ __forceinline__ static float g(float r, const KArgs&) { return r * (1.f - r); }
+  // sig(z)(1 - sig(z)) = r - r^2 in one fma; alpha / denom is in rmul
+  __device__ __forceinline__ static float g(float r, const KArgs&) { return __builtin_fmaf(-r, r, r); }
 };
 
 template <> struct Cap<3, true> {
