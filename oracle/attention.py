@@ -237,26 +237,41 @@ def forward(q, k, v, p: Params, temperature=None, segment_ids=None, ranker_bound
 # Backward
 # ---------------------------------------------------------------------------
 
-def _ds_block(st, q, v, do, b, hq, rr, p: Params, delta_rows):
-    """dS for one row block: dS' = P (dP - delta) + w P LSE, then
-    dS = dS' * temp * cap'(s) * sm_scale."""
+def _dsp_block(st, v, do, b, hq, rr, p: Params, delta_rows):
+    """dS' = dF/dS' for one row block: P (dP - delta) + w P LSE."""
     dP = do[b, rr, hq, :] @ v[b, :, st["g"], :].T
     lse = np.where(st["any"], st["lse"], 0.0)
-    dsp = st["P"] * (dP - delta_rows[:, None]) + p.z_loss_weight * st["P"] * lse[:, None]
+    return st["P"] * (dP - delta_rows[:, None]) + p.z_loss_weight * st["P"] * lse[:, None]
+
+
+def _ds_block(st, q, v, do, b, hq, rr, p: Params, delta_rows):
+    """dS for one row block: dS = dS' * temp * cap'(s) * sm_scale."""
+    dsp = _dsp_block(st, v, do, b, hq, rr, p, delta_rows)
     dcap = cap_derivative(st["s"], p.cap_method, p.cap, p.alpha, p.beta)
     return dsp * st["t"][:, None] * dcap * p.sm_scale
+
+
+def _dtemp_block(st, v, do, b, hq, rr, p: Params, delta_rows):
+    """One query head's share of the temperature gradient of the rows rr.
+    S'_ij = temp_i c_ij, so dF/dtemp_i gets sum_j dS'_ij c_ij from every head."""
+    dsp = _dsp_block(st, v, do, b, hq, rr, p, delta_rows)
+    return np.sum(dsp * np.where(st["vis"], st["c"], 0.0), axis=1)
 
 
 def backward(q, k, v, do, p: Params, temperature=None, segment_ids=None, ranker_bounds=None,
              row_chunk: int = 512, groups=None):
     """Gradients of F = sum(O * dO) + (w/2) * sum over rows of LSE^2.
 
-    Returns dict(delta (B,Hq,L), dq (B,L,Hq,D), dk, dv (B,L,Hkv,D), o, m, l).
+    Returns dict(delta (B,Hq,L), dq (B,L,Hq,D), dk, dv (B,L,Hkv,D), dtemp (B,L),
+    o, m, l).
     delta_i = sum_d O_id dO_id; dP = dO V^T; dS as in ``_ds_block``;
     dQ = dS K; dK = sum over the query heads of a group of dS^T Q;
-    dV = likewise of P^T dO.
+    dV = likewise of P^T dO; dtemp_i = sum over the query heads of
+    sum_j dS'_ij c_ij (the temperature multiplies the capped logits, and one
+    temperature row serves every head).
     ``groups`` restricts the work to a list of (b, kv_head) pairs (every query
-    head of each group); entries outside are left NaN.
+    head of each group); entries outside are left NaN, and so is dtemp unless
+    every group is included.
     """
     B, L, Hq, Hkv, D, G = _check(q, k, v)
     if groups is None:
@@ -273,6 +288,8 @@ def backward(q, k, v, do, p: Params, temperature=None, segment_ids=None, ranker_
     dq = np.full((B, L, Hq, D), np.nan)
     dk = np.full((B, L, Hkv, D), np.nan)
     dv = np.full((B, L, Hkv, D), np.nan)
+    full = sorted(groups) == [(b, g) for b in range(B) for g in range(Hkv)]
+    dtemp = np.zeros((B, L)) if full else np.full((B, L), np.nan)
     rows = np.arange(L)
     for b, g0 in groups:
         dk[b, :, g0] = 0.0
@@ -286,7 +303,9 @@ def backward(q, k, v, do, p: Params, temperature=None, segment_ids=None, ranker_
                 dq[b, rr, hq, :] = ds @ k[b, :, g, :]
                 dk[b, :, g, :] += ds.T @ q[b, rr, hq, :]
                 dv[b, :, g, :] += st["P"].T @ do[b, rr, hq, :]
-    return dict(delta=delta, dq=dq, dk=dk, dv=dv, o=o, m=m, l=l)
+                if full:
+                    dtemp[b, rr] += _dtemp_block(st, v, do, b, hq, rr, p, delta[b, hq, rr])
+    return dict(delta=delta, dq=dq, dk=dk, dv=dv, dtemp=dtemp, o=o, m=m, l=l)
 
 
 def preprocess(o, do):
@@ -298,14 +317,16 @@ def preprocess(o, do):
 
 def dq_rows(q, k, v, do, p: Params, b, hq, rows, temperature=None, segment_ids=None,
             ranker_bounds=None):
-    """dQ for selected rows of one (b, hq); also returns O, m, l, delta of those rows."""
+    """dQ for selected rows of one (b, hq); also returns O, m, l, delta of those
+    rows and this head's share of their temperature gradient (dtemp_h)."""
     B, L, Hq, Hkv, D, G = _check(q, k, v)
     rows = np.asarray(rows)
     st = _row_block(q, k, v, b, hq, rows, p, G, temperature, segment_ids, ranker_bounds)
     o_r = st["P"] @ v[b, :, st["g"], :]
     delta_r = np.sum(o_r * do[b, rows, hq, :], axis=1)
     ds = _ds_block(st, q, v, do, b, hq, rows, p, delta_r)
-    return dict(dq=ds @ k[b, :, st["g"], :], o=o_r, m=st["m"], l=st["l"], delta=delta_r)
+    return dict(dq=ds @ k[b, :, st["g"], :], o=o_r, m=st["m"], l=st["l"], delta=delta_r,
+                dtemp_h=_dtemp_block(st, v, do, b, hq, rows, p, delta_r))
 
 
 def dkv_keys(q, k, v, do, p: Params, b, g, keys, temperature=None, segment_ids=None,
@@ -341,3 +362,24 @@ def unmasked_pairs(L: int, p: Params, segment_ids=None, ranker_bounds=None, B: i
             total += int(visible(rr, L, p, None if segment_ids is None else segment_ids[b],
                                  None if ranker_bounds is None else ranker_bounds[b]).sum())
     return total
+
+
+def ranker_bounds_from_segments(segment_ids, history_id: int, candidate_id: int):
+    """Ranker bounds (B, 4) = [hl, hu, cl, cu] from segment ids (B, L).
+
+    The mosaic_backward.py page's test marks history positions and candidate
+    positions with two reserved segment ids and expects the kernels' ranker
+    bounds to follow from them; the ids' values and the mapping are not
+    printed.  Reading: [hl, hu) is the smallest interval holding every
+    position whose id is ``history_id`` ([0, 0) if there is none), and the
+    same for the candidates.  For contiguous runs that is the run itself."""
+    seg = np.asarray(segment_ids)
+    B = seg.shape[0]
+    out = np.zeros((B, 4), dtype=np.int32)
+    for b in range(B):
+        for k, ident in enumerate((history_id, candidate_id)):
+            pos = np.nonzero(seg[b] == ident)[0]
+            if pos.size:
+                out[b, 2 * k] = pos.min()
+                out[b, 2 * k + 1] = pos.max() + 1
+    return out

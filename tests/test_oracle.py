@@ -8,7 +8,7 @@ import torch
 import torch.nn.functional as F
 
 from oracle import (Params, backward, cap_derivative, cap_forward, dkv_keys, dq_rows, forward,
-                    sigmoid, unmasked_pairs, visible)
+                    ranker_bounds_from_segments, sigmoid, unmasked_pairs, visible)
 
 pytestmark = pytest.mark.filterwarnings("ignore::RuntimeWarning")
 
@@ -218,7 +218,10 @@ def fd_check(q, k, v, do, p, temp, seg, rb, n_samples=60, seed=0, rtol=2e-6, eps
     res = backward(q, k, v, do, p, temp, seg, rb)
     rng = np.random.default_rng(seed)
     scale = max(np.abs(res[n]).max() for n in ("dq", "dk", "dv"))
-    for name, arr in (("dq", q), ("dk", k), ("dv", v)):
+    pairs = [("dq", q), ("dk", k), ("dv", v)]
+    if temp is not None:
+        pairs.append(("dtemp", temp))
+    for name, arr in pairs:
         flat = arr.reshape(-1)
         idx = rng.choice(flat.size, size=min(n_samples, flat.size), replace=False)
         for t in idx:
@@ -230,7 +233,8 @@ def fd_check(q, k, v, do, p, temp, seg, rb, n_samples=60, seed=0, rtol=2e-6, eps
             flat[t] = old
             fd = (fp - fm) / (2 * eps)
             an = res[name].reshape(-1)[t]
-            assert abs(fd - an) <= rtol * scale + 1e-7 * abs(fd), (name, t, fd, an)
+            sc = scale if name != "dtemp" else max(scale, np.abs(res["dtemp"]).max())
+            assert abs(fd - an) <= rtol * sc + 1e-7 * abs(fd), (name, t, fd, an)
 
 
 @pytest.mark.parametrize("cap", CAPS)
@@ -438,3 +442,92 @@ def test_cap_golden_closed_forms():
         assert cap_forward(s, *args)[0] == pytest.approx(c["value"], rel=1e-11, abs=1e-12), c
         if "slope" in c:
             assert cap_derivative(s, *args)[0] == pytest.approx(c["slope"], rel=1e-11), c
+
+
+# ---------------------------------------------------------------------------
+# Temperature gradient and ranker bounds from segment ids
+# ---------------------------------------------------------------------------
+
+def test_dtemp_equals_dq_dot_q_without_cap():
+    """Without a cap, temp_i scales row i of Q: t_i * dtemp_i = sum_h dQ_ih . Q_ih."""
+    rng = np.random.default_rng(21)
+    B, L, Hq, Hkv, D = 2, 16, 4, 2, 8
+    q, do = rnd(rng, B, L, Hq, D), rnd(rng, B, L, Hq, D)
+    k, v = rnd(rng, B, L, Hkv, D), rnd(rng, B, L, Hkv, D)
+    temp = rng.uniform(0.5, 1.5, size=(B, L))
+    p = Params(0.6, causal=True, window_len=6, z_loss_weight=0.25)
+    res = backward(q, k, v, do, p, temp)
+    lhs = temp * res["dtemp"]
+    rhs = np.einsum("blhd,blhd->bl", res["dq"], q)
+    assert np.allclose(lhs, rhs, rtol=1e-12, atol=1e-13)
+    assert np.abs(res["dtemp"]).max() > 1e-3
+
+
+def test_dtemp_rows_helper_sums_to_backward():
+    rng = np.random.default_rng(22)
+    B, L, Hq, Hkv, D = 1, 12, 4, 2, 8
+    q, do = rnd(rng, B, L, Hq, D), rnd(rng, B, L, Hq, D)
+    k, v = rnd(rng, B, L, Hkv, D), rnd(rng, B, L, Hkv, D)
+    temp = rng.uniform(0.5, 1.5, size=(B, L))
+    p = Params(0.5, causal=True, cap_method="alsc", cap=6.0, alpha=3.0, beta=0.25,
+               z_loss_weight=0.1)
+    res = backward(q, k, v, do, p, temp)
+    rows = np.array([0, 3, 7, 11])
+    tot = sum(dq_rows(q, k, v, do, p, 0, h, rows, temp)["dtemp_h"] for h in range(Hq))
+    assert np.allclose(tot, res["dtemp"][0, rows], rtol=1e-12, atol=1e-14)
+    # a row restricted backward leaves dtemp undefined
+    part = backward(q, k, v, do, p, temp, groups=[(0, 0)])
+    assert np.all(np.isnan(part["dtemp"]))
+
+
+def test_dtemp_of_fully_masked_row_is_zero():
+    rng = np.random.default_rng(23)
+    B, L, Hq, D = 1, 8, 2, 4
+    q, do = rnd(rng, B, L, Hq, D), rnd(rng, B, L, Hq, D)
+    k, v = rnd(rng, B, L, Hq, D), rnd(rng, B, L, Hq, D)
+    rb = np.array([[2, 5, 5, 7]])        # rows 0, 1 and 7 see nothing
+    res = backward(q, k, v, do, Params(0.5, z_loss_weight=0.2), rng.uniform(0.5, 1.5, (B, L)),
+                   None, rb)
+    assert np.all(res["dtemp"][0, [0, 1, 7]] == 0.0)
+    assert np.all(res["dtemp"][0, 2:7] != 0.0)
+
+
+def _bounds_by_loop(seg, hid, cid):
+    out = []
+    for row in seg:
+        b = []
+        for ident in (hid, cid):
+            lo, hi = None, None
+            for i, x in enumerate(row):
+                if x == ident:
+                    lo = i if lo is None else lo
+                    hi = i + 1
+            b += [0, 0] if lo is None else [lo, hi]
+        out.append(b)
+    return np.array(out, dtype=np.int32)
+
+
+def test_ranker_bounds_page_test_pattern():
+    """The page's test: the first half of each row is history, the rest candidates."""
+    L, HID, CID = 128, 7, 9
+    seg = np.zeros((2, L), dtype=np.int32)
+    seg[:, :L // 2] = HID
+    seg[:, L // 2:] = CID
+    assert ranker_bounds_from_segments(seg, HID, CID).tolist() == [[0, 64, 64, 128]] * 2
+
+
+def test_ranker_bounds_edge_cases_and_brute_force():
+    HID, CID = 3, 5
+    seg = np.array([[0, 0, 0, 0, 0, 0],      # neither id
+                    [3, 3, 3, 3, 3, 3],      # history only
+                    [5, 0, 0, 0, 0, 0],      # one candidate at the start
+                    [0, 0, 0, 0, 0, 3],      # one history position at the end
+                    [3, 0, 3, 5, 0, 5]],     # non-contiguous: the smallest covering interval
+                   dtype=np.int32)
+    got = ranker_bounds_from_segments(seg, HID, CID)
+    assert got.tolist() == [[0, 0, 0, 0], [0, 6, 0, 0], [0, 0, 0, 1], [5, 6, 0, 0],
+                            [0, 3, 3, 6]]
+    rng = np.random.default_rng(24)
+    for _ in range(20):
+        s = rng.integers(0, 8, size=(3, int(rng.integers(1, 40)))).astype(np.int32)
+        assert np.array_equal(ranker_bounds_from_segments(s, 2, 6), _bounds_by_loop(s, 2, 6))
