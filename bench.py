@@ -34,10 +34,10 @@ HBM_GBPS = 8000.0
 KERNEL_SOURCES = ["attn_bf16.hip", "attn_bf16.h", "attn_device.h", "attn_tiles.h",
                   "attn_internal.h", "attn_bwd_common.h", "attn_preprocess.hip"]
 MEASURED_TRAFFIC = {
-    ("92eb2e4ed7c0078f", 5, 1): {"attn_fwd": (452593 * 2.0 + 169416) * 1024,
-                                 "attn_bwd_preprocess": (98332 * 2.0 + 4097) * 1024,
-                                 "attn_bwd_dq": (441095 * 2.0 + 131072) * 1024,
-                                 "attn_bwd_dkv": (376021 * 2.0 + 266242) * 1024},
+    ("41a5c5f9271ae676", 5, 0): {"attn_fwd": (423134 * 2.0 + 166275) * 1024,
+                                 "attn_bwd_preprocess": (98333 * 2.0 + 4097) * 1024,
+                                 "attn_bwd_dq": (433227 * 2.0 + 131072) * 1024,
+                                 "attn_bwd_dkv": (363677 * 2.0 + 266240) * 1024},
 }
 
 

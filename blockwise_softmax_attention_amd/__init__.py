@@ -74,7 +74,9 @@ _P = ctypes.c_void_p
 _FN_SIGS = {
     "attn_fwd": [ctypes.POINTER(_CParams), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
     "attn_bwd_preprocess": [ctypes.POINTER(_CParams), _P, _P, _P, _P],
-    "attn_bwd_dq": [ctypes.POINTER(_CParams), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
+    "attn_bwd_dq": [ctypes.POINTER(_CParams), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
+    "attn_reduce_heads": [ctypes.POINTER(_CParams), _P, _P, _P],
+    "attn_ranker_bounds": [_P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P, _P],
     "attn_bwd_dkv": [ctypes.POINTER(_CParams), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
     "attn_plan_count": [ctypes.POINTER(_CParams), _P, _P, ctypes.POINTER(ctypes.c_int64),
                         ctypes.POINTER(ctypes.c_int64)],
@@ -163,9 +165,15 @@ def attn_bwd_preprocess(p: AttnParams, o, d_o, delta=None, stream=None):
 
 
 def attn_bwd_dq(p: AttnParams, q, k, v, d_o, m, l, delta, temperature=None, segment_ids=None,
-                ranker_bounds=None, dq=None, stream=None):
+                ranker_bounds=None, dq=None, dtemp_h=None, stream=None):
+    """Returns dq; with a (B, Hq, L) float tensor dtemp_h (or dtemp_h=True to
+    allocate one) also fills each head's share of the temperature gradient
+    and returns (dq, dtemp_h)."""
     dq = torch.empty((p.batch, p.seq_len, p.q_heads, p.head_dim), dtype=torch.float32,
                      device=q.device) if dq is None else dq
+    want = dtemp_h is not None and dtemp_h is not False
+    if dtemp_h is True:
+        dtemp_h = torch.empty((p.batch, p.q_heads, p.seq_len), dtype=torch.float32, device=q.device)
     dt = _in_dtype(p)
     cp = p.to_c()
     _check(load_library().attn_bwd_dq(
@@ -173,8 +181,28 @@ def attn_bwd_dq(p: AttnParams, q, k, v, d_o, m, l, delta, temperature=None, segm
         _ptr(temperature, "temperature", torch.float32), _ptr(segment_ids, "segment_ids", torch.int32),
         _ptr(ranker_bounds, "ranker_bounds", torch.int32), _ptr(d_o, "d_o", dt),
         _ptr(m, "m", torch.float32), _ptr(l, "l", torch.float32), _ptr(delta, "delta", torch.float32),
-        _ptr(dq, "dq", torch.float32), _stream(stream)))
-    return dq
+        _ptr(dq, "dq", torch.float32), _ptr(dtemp_h if want else None, "dtemp_h", torch.float32),
+        _stream(stream)))
+    return (dq, dtemp_h) if want else dq
+
+
+def attn_reduce_heads(p: AttnParams, x, out=None, stream=None):
+    """out (B, L) = sum over the Hq heads of x (B, Hq, L), in head order."""
+    out = torch.empty((p.batch, p.seq_len), dtype=torch.float32, device=x.device) if out is None else out
+    cp = p.to_c()
+    _check(load_library().attn_reduce_heads(ctypes.byref(cp), _ptr(x, "x", torch.float32),
+                                            _ptr(out, "out", torch.float32), _stream(stream)))
+    return out
+
+
+def attn_ranker_bounds(segment_ids, history_id: int, candidate_id: int, out=None, stream=None):
+    """Ranker bounds (B, 4) int32 from segment ids (B, L) int32 on the GPU."""
+    B, L = segment_ids.shape
+    out = torch.empty((B, 4), dtype=torch.int32, device=segment_ids.device) if out is None else out
+    _check(load_library().attn_ranker_bounds(
+        _ptr(segment_ids, "segment_ids", torch.int32), int(B), int(L), int(history_id),
+        int(candidate_id), _ptr(out, "ranker_bounds", torch.int32), _stream(stream)))
+    return out
 
 
 def attn_bwd_dkv(p: AttnParams, q, k, v, d_o, m, l, delta, temperature=None, segment_ids=None,
@@ -215,15 +243,21 @@ def attn_plan_count(p: AttnParams, segment_ids=None, ranker_bounds=None):
 
 
 def attention_forward_backward(p: AttnParams, q, k, v, d_o, temperature=None, segment_ids=None,
-                               ranker_bounds=None, stream=None):
-    """One pass of the whole path: forward, then preprocess, dQ and dK/dV."""
+                               ranker_bounds=None, dtemp: bool = False, stream=None):
+    """One pass of the whole path: forward, then preprocess, dQ and dK/dV
+    (and, with dtemp=True, the temperature gradient (B, L))."""
     o, m, l = attn_fwd(p, q, k, v, temperature, segment_ids, ranker_bounds, stream=stream)
     delta = attn_bwd_preprocess(p, o, d_o, stream=stream)
-    dq = attn_bwd_dq(p, q, k, v, d_o, m, l, delta, temperature, segment_ids, ranker_bounds,
-                     stream=stream)
+    res = attn_bwd_dq(p, q, k, v, d_o, m, l, delta, temperature, segment_ids, ranker_bounds,
+                      dtemp_h=True if dtemp else None, stream=stream)
+    dq, dtemp_h = res if dtemp else (res, None)
     dk, dv = attn_bwd_dkv(p, q, k, v, d_o, m, l, delta, temperature, segment_ids, ranker_bounds,
                           stream=stream)
-    return dict(o=o, m=m, l=l, delta=delta, dq=dq, dk=dk, dv=dv)
+    out = dict(o=o, m=m, l=l, delta=delta, dq=dq, dk=dk, dv=dv)
+    if dtemp:
+        out["dtemp_h"] = dtemp_h
+        out["dtemp"] = attn_reduce_heads(p, dtemp_h, stream=stream)
+    return out
 
 
 def params_for(w, precise_ds: bool = True) -> AttnParams:

@@ -21,7 +21,7 @@ LIB = os.path.join(PKG, "libattn.so")
 ROOT = os.path.dirname(PKG)
 
 SOURCES = ["attn_api.hip", "attn_fwd.hip", "attn_preprocess.hip", "attn_dq.hip", "attn_dkv.hip",
-           "attn_bf16.hip"]
+           "attn_bf16.hip", "attn_aux.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

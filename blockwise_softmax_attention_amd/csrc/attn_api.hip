@@ -225,9 +225,11 @@ static attn_status check_bwd_inputs(const attn_params* p, const void* q, const v
 attn_status attn_bwd_dq(const attn_params* p, const void* q, const void* k, const void* v,
                         const float* temperature, const int32_t* segment_ids,
                         const int32_t* ranker_bounds, const void* d_o, const float* m,
-                        const float* l, const float* delta, float* dq, void* stream) {
+                        const float* l, const float* delta, float* dq, float* dtemp_h,
+                        void* stream) {
   ATTN_TRY(check_bwd_inputs(p, q, k, v, temperature, segment_ids, ranker_bounds, d_o, m, l, delta));
   ATTN_TRY(check_ptr(dq, "dq", 16));
+  ATTN_TRY(check_opt(dtemp_h, "dtemp_h"));
   attn::KArgs a = make_args(p, temperature, segment_ids, ranker_bounds);
   a.q = q;
   a.k = k;
@@ -237,9 +239,33 @@ attn_status attn_bwd_dq(const attn_params* p, const void* q, const void* k, cons
   a.l_in = l;
   a.delta_in = delta;
   a.out0 = dq;
+  a.out3 = dtemp_h;
   a.n_items = a.B * a.Hq * a.n_q_tiles;
   return hip_status(attn::launch_dq(a, p->dtype, p->head_dim, effective_cap(p), (hipStream_t)stream),
                     "attn_bwd_dq launch");
+}
+
+attn_status attn_reduce_heads(const attn_params* p, const float* x, float* out, void* stream) {
+  ATTN_TRY(check_params(p));
+  ATTN_TRY(check_ptr(x, "x", 4));
+  ATTN_TRY(check_ptr(out, "out", 4));
+  return hip_status(attn::launch_reduce_heads(x, out, p->batch, p->q_heads, p->seq_len,
+                                              (hipStream_t)stream),
+                    "attn_reduce_heads launch");
+}
+
+attn_status attn_ranker_bounds(const int32_t* segment_ids, int32_t batch, int32_t seq_len,
+                               int32_t history_id, int32_t candidate_id, int32_t* ranker_bounds,
+                               void* stream) {
+  if (batch < 1 || seq_len < 1) return fail(ATTN_ERR_SHAPE, "batch and seq_len must be >= 1");
+  if (seq_len > ATTN_MAX_SEQ_LEN) return fail(ATTN_ERR_SHAPE, "seq_len exceeds ATTN_MAX_SEQ_LEN");
+  if (history_id == candidate_id)
+    return fail(ATTN_ERR_PARAM, "history_id and candidate_id must differ");
+  ATTN_TRY(check_ptr(segment_ids, "segment_ids", 4));
+  ATTN_TRY(check_ptr(ranker_bounds, "ranker_bounds", 4));
+  return hip_status(attn::launch_ranker_bounds(segment_ids, ranker_bounds, batch, seq_len, history_id,
+                                               candidate_id, (hipStream_t)stream),
+                    "attn_ranker_bounds launch");
 }
 
 attn_status attn_bwd_dkv(const attn_params* p, const void* q, const void* k, const void* v,

@@ -327,29 +327,35 @@ __global__ __launch_bounds__(NTHREADS, ATTN_FWD_WAVES_PER_SIMD) void fwd_bf16_ke
 // ---------------------------------------------------------------------------
 // dQ
 // ---------------------------------------------------------------------------
-template <bool MASKED, bool SEG, int CAP, int NKB>
+// DT: also accumulate this row's share of the temperature gradient,
+// sum_j dS'_ij c_ij with c = ln2 (kmul f + kadd) (the ln2 is applied once at
+// the end).
+template <bool MASKED, bool SEG, int CAP, bool DT, int NKB>
 __device__ __forceinline__ void dq_elementwise(f32x16 (&s)[NKB], const f32x16 (&dp)[NKB], const KArgs& a,
                                                const RowC& rc, float dlt, const QMask& qm, int k0,
-                                               int hh, const int* sseg, int seg_q) {
+                                               int hh, const int* sseg, int seg_q, float& tacc) {
   using CapF = Cap<CAP, false>;
 #pragma unroll
   for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       float aux;
-      float p = fast_exp2(__builtin_fmaf(CapF::f(s[kb][r], a, aux), rc.Kf, rc.C2));
+      const float fx = CapF::f(s[kb][r], a, aux);
+      float p = fast_exp2(__builtin_fmaf(fx, rc.Kf, rc.C2));
       if (MASKED) {
         const int koff = kb * 32 + prow(r, hh);
         bool vis = qmask_vis(qm, k0 + koff);
         if (SEG) vis = vis && sseg[koff] == seg_q;
         p = vis ? p : 0.f;
       }
-      s[kb][r] = (p * (dp[kb][r] - dlt)) * (rc.R * CapF::g(aux, a));
+      const float dsp = p * (dp[kb][r] - dlt);
+      if (DT) tacc = __builtin_fmaf(dsp, __builtin_fmaf(fx, a.kmul, a.kadd), tacc);
+      s[kb][r] = dsp * (rc.R * CapF::g(aux, a));
     }
   }
 }
 
-template <int D, int CAP, bool PRECISE>
+template <int D, int CAP, bool PRECISE, bool DT>
 __global__ __launch_bounds__(NTHREADS, 2) void dq_bf16_kernel(KArgs a) {
   constexpr int BN = BNQ16;
   using KT = BTile<BN, D, NWAVES, ATTN_LAUNDER_DQ>;
@@ -430,6 +436,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void dq_bf16_kernel(KArgs a) {
     if (has_seg && tid < BN) sSeg[st][tid] = pseg;
   };
 
+  float tacc = 0.f;
   f32x16 dqacc[NDB];
 #pragma unroll
   for (int i = 0; i < NDB; ++i) dqacc[i] = f32x16{};
@@ -489,11 +496,11 @@ __global__ __launch_bounds__(NTHREADS, 2) void dq_bf16_kernel(KArgs a) {
     // branch on it instead of running every variant under an exec mask
     const int tcls = __builtin_amdgcn_readfirstlane(tile_class(it.qw0, it.qw0 + 32, k0, k0 + BN, ms));
     if (tcls == TILE_FULL) {
-      dq_elementwise<false, false, CAP>(sacc, pacc, a, rc, dlt, qm, k0, hh, nullptr, 0);
+      dq_elementwise<false, false, CAP, DT>(sacc, pacc, a, rc, dlt, qm, k0, hh, nullptr, 0, tacc);
     } else if (!seg_any) {
-      dq_elementwise<true, false, CAP>(sacc, pacc, a, rc, dlt, qm, k0, hh, nullptr, 0);
+      dq_elementwise<true, false, CAP, DT>(sacc, pacc, a, rc, dlt, qm, k0, hh, nullptr, 0, tacc);
     } else {
-      dq_elementwise<true, true, CAP>(sacc, pacc, a, rc, dlt, qm, k0, hh, sSeg[st], seg_q);
+      dq_elementwise<true, true, CAP, DT>(sacc, pacc, a, rc, dlt, qm, k0, hh, sSeg[st], seg_q, tacc);
     }
 #pragma unroll
     for (int t = 0; t < BN / 16; ++t) {
@@ -517,6 +524,10 @@ __global__ __launch_bounds__(NTHREADS, 2) void dq_bf16_kernel(KArgs a) {
     j = jn;
   }
 
+  if (DT) {
+    const float tot = half_sum(tacc);   // the row's two key halves
+    if (row_ok && hh == 0) a.out3[((long)b * a.Hq + it.hq) * L + qrow] = tot * LN2_F;
+  }
   if (row_ok) {
     float* drow = a.out0 + ((long)(b * L + qrow) * a.Hq + it.hq) * D;
 #pragma unroll
@@ -839,11 +850,20 @@ static void fwd_bf16_d(const KArgs& a, int cap, hipStream_t s) {
 template <int D, bool P>
 static void dq_bf16_d(const KArgs& a, int cap, hipStream_t s) {
   dim3 grid(a.n_items), block(NTHREADS);
+  if (a.out3 != nullptr) {
+    switch (cap) {
+      case 0: hipLaunchKernelGGL((dq_bf16_kernel<D, 0, P, true>), grid, block, 0, s, a); break;
+      case 1: hipLaunchKernelGGL((dq_bf16_kernel<D, 1, P, true>), grid, block, 0, s, a); break;
+      case 2: hipLaunchKernelGGL((dq_bf16_kernel<D, 2, P, true>), grid, block, 0, s, a); break;
+      default: hipLaunchKernelGGL((dq_bf16_kernel<D, 3, P, true>), grid, block, 0, s, a); break;
+    }
+    return;
+  }
   switch (cap) {
-    case 0: hipLaunchKernelGGL((dq_bf16_kernel<D, 0, P>), grid, block, 0, s, a); break;
-    case 1: hipLaunchKernelGGL((dq_bf16_kernel<D, 1, P>), grid, block, 0, s, a); break;
-    case 2: hipLaunchKernelGGL((dq_bf16_kernel<D, 2, P>), grid, block, 0, s, a); break;
-    default: hipLaunchKernelGGL((dq_bf16_kernel<D, 3, P>), grid, block, 0, s, a); break;
+    case 0: hipLaunchKernelGGL((dq_bf16_kernel<D, 0, P, false>), grid, block, 0, s, a); break;
+    case 1: hipLaunchKernelGGL((dq_bf16_kernel<D, 1, P, false>), grid, block, 0, s, a); break;
+    case 2: hipLaunchKernelGGL((dq_bf16_kernel<D, 2, P, false>), grid, block, 0, s, a); break;
+    default: hipLaunchKernelGGL((dq_bf16_kernel<D, 3, P, false>), grid, block, 0, s, a); break;
   }
 }
 

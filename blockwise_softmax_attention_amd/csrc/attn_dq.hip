@@ -35,7 +35,9 @@ template <typename T, int D> struct DqCfg {
   static constexpr int BN = 32;   // keys per streamed tile
 };
 
-template <typename T, int D, int CAP, bool PRECISE>
+// DT: also accumulate this head's share of the temperature gradient,
+// dtemp_i = sum_j dS'_ij c_ij with c the capped logit, c = ln2 (kmul f + kadd).
+template <typename T, int D, int CAP, bool PRECISE, bool DT>
 __global__ __launch_bounds__(NTHREADS, 2) void dq_kernel(KArgs a) {
   constexpr int BN = DqCfg<T, D>::BN;
   constexpr bool ACC = sizeof(T) == 4;
@@ -141,6 +143,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void dq_kernel(KArgs a) {
   };
 
   KIO kio, vio;
+  float tacc = 0.f;
   f32x16 dqacc[NDB];
 #pragma unroll
   for (int i = 0; i < NDB; ++i) dqacc[i] = f32x16{};
@@ -182,14 +185,17 @@ __global__ __launch_bounds__(NTHREADS, 2) void dq_kernel(KArgs a) {
       for (int r = 0; r < 16; ++r) {
         float aux;
         const float x = sacc[kb][r];
-        float p = fast_exp2(__builtin_fmaf(CapF::f(x, a, aux), rc.Kf, rc.C2));
+        const float fx = CapF::f(x, a, aux);
+        float p = fast_exp2(__builtin_fmaf(fx, rc.Kf, rc.C2));
         if (!full) {
           const int koff = kb * 32 + prow(r, hh);
           bool vis = pair_visible(qrow, k0 + koff, ms);
           if (has_seg) vis = vis && (sSeg[buf][koff] == seg_q);
           p = vis ? p : 0.f;
         }
-        sacc[kb][r] = p * (pacc[kb][r] - dlt) * rc.R * CapF::g(aux, a);
+        const float dsp = p * (pacc[kb][r] - dlt);
+        if (DT) tacc = __builtin_fmaf(dsp, __builtin_fmaf(fx, a.kmul, a.kadd), tacc);
+        sacc[kb][r] = dsp * rc.R * CapF::g(aux, a);
       }
     }
     // dQ^T += K^T dS^T
@@ -220,6 +226,11 @@ __global__ __launch_bounds__(NTHREADS, 2) void dq_kernel(KArgs a) {
     j = jn;
   }
 
+  if (DT) {
+    // lanes l and l + 32 hold the same query's two key halves
+    const float tot = tacc + __shfl_xor(tacc, 32);
+    if (row_ok && hh == 0) a.out3[((long)b * a.Hq + hq) * L + qrow] = tot * LN2_F;
+  }
   if (row_ok) {
     float* drow = a.out0 + ((long)(b * L + qrow) * a.Hq + hq) * D;
 #pragma unroll
@@ -235,21 +246,22 @@ __global__ __launch_bounds__(NTHREADS, 2) void dq_kernel(KArgs a) {
   }
 }
 
-template <typename T, int D, bool P>
+template <typename T, int D, bool P, bool DT>
 static void dq_cap(const KArgs& a, int cap, hipStream_t s) {
   dim3 grid(a.n_items), block(NTHREADS);
   switch (cap) {
-    case 0: hipLaunchKernelGGL((dq_kernel<T, D, 0, P>), grid, block, 0, s, a); break;
-    case 1: hipLaunchKernelGGL((dq_kernel<T, D, 1, P>), grid, block, 0, s, a); break;
-    case 2: hipLaunchKernelGGL((dq_kernel<T, D, 2, P>), grid, block, 0, s, a); break;
-    default: hipLaunchKernelGGL((dq_kernel<T, D, 3, P>), grid, block, 0, s, a); break;
+    case 0: hipLaunchKernelGGL((dq_kernel<T, D, 0, P, DT>), grid, block, 0, s, a); break;
+    case 1: hipLaunchKernelGGL((dq_kernel<T, D, 1, P, DT>), grid, block, 0, s, a); break;
+    case 2: hipLaunchKernelGGL((dq_kernel<T, D, 2, P, DT>), grid, block, 0, s, a); break;
+    default: hipLaunchKernelGGL((dq_kernel<T, D, 3, P, DT>), grid, block, 0, s, a); break;
   }
 }
 
 hipError_t launch_dq(const KArgs& a, int dtype, int head_dim, int cap, hipStream_t s) {
   if (dtype == 1) return launch_dq_bf16(a, head_dim, cap, s);
-  if (head_dim == 64) dq_cap<float, 64, false>(a, cap, s);
-  else dq_cap<float, 128, false>(a, cap, s);
+  const bool dt = a.out3 != nullptr;
+  if (head_dim == 64) dt ? dq_cap<float, 64, false, true>(a, cap, s) : dq_cap<float, 64, false, false>(a, cap, s);
+  else dt ? dq_cap<float, 128, false, true>(a, cap, s) : dq_cap<float, 128, false, false>(a, cap, s);
   return hipGetLastError();
 }
 

@@ -32,6 +32,7 @@ struct KArgs {
   float* out0;             // fwd: O      dq: dQ    dkv: dK   pre: delta
   float* out1;             // fwd: m                dkv: dV
   float* out2;             // fwd: l
+  float* out3;             // dq: this head's share of the temperature gradient (B, Hq, L), or null
   int B, L, Hq, Hkv, G;
   int causal, window;
   float sm_scale;
@@ -59,6 +60,9 @@ hipError_t launch_fwd(const KArgs& a, int dtype, int head_dim, int cap, hipStrea
 hipError_t launch_preprocess(const KArgs& a, int dtype, int head_dim, hipStream_t s);
 hipError_t launch_dq(const KArgs& a, int dtype, int head_dim, int cap, hipStream_t s);
 hipError_t launch_dkv(const KArgs& a, int dtype, int head_dim, int cap, hipStream_t s);
+hipError_t launch_reduce_heads(const float* x, float* out, int B, int H, int L, hipStream_t s);
+hipError_t launch_ranker_bounds(const int32_t* seg, int32_t* bounds, int B, int L, int32_t hist_id,
+                                int32_t cand_id, hipStream_t s);
 int fwd_key_tile(int dtype, int head_dim);   // keys per forward tile
 // bfloat16 kernels (attn_bf16.hip)
 hipError_t launch_fwd_bf16(const KArgs& a, int head_dim, int cap, hipStream_t s);

@@ -116,11 +116,38 @@ attn_status attn_bwd_preprocess(const attn_params* params, const float* o, const
                                 float* delta, void* stream);
 
 /* dQ (triton_kernels.py page, make_triton_backward_kernel_dq): recomputes P
- * from m and l and writes dq (B, L, Hq, D). */
+ * from m and l and writes dq (B, L, Hq, D).
+ * dtemp_h (optional, NULL skips it): (B, Hq, L) float, 4-byte aligned; row i
+ * of head h receives that head's share of the temperature gradient,
+ *   dtemp_h[b,h,i] = sum_j dS'_ij c_ij   (c = cap(sm_scale q.k), dS' as above),
+ * since S' = temp * c.  The gradient of temperature[b,i] is the sum over h
+ * (attn_reduce_heads).  The pages' orchestrator (mosaic_backward.py page,
+ * mosaic_attention_backward) returns a dtemp slot filled with zeros; this is
+ * the actual derivative. */
 attn_status attn_bwd_dq(const attn_params* params, const void* q, const void* k, const void* v,
                         const float* temperature, const int32_t* segment_ids,
                         const int32_t* ranker_bounds, const void* d_o, const float* m,
-                        const float* l, const float* delta, float* dq, void* stream);
+                        const float* l, const float* delta, float* dq, float* dtemp_h,
+                        void* stream);
+
+/* out[b,i] = sum over h = 0 .. Hq-1 of x[b,h,i] in that fixed order (no
+ * atomics), for x (B, Hq, L) and out (B, L) float, both 4-byte aligned; B, Hq
+ * and L come from params.  Turns the per-head dtemp_h of attn_bwd_dq into the
+ * gradient of the (B, L) temperature. */
+attn_status attn_reduce_heads(const attn_params* params, const float* x, float* out, void* stream);
+
+/* Ranker bounds from segment ids, on the device (the mosaic_backward.py page's
+ * test marks history and candidate positions with two reserved segment ids;
+ * the page prints neither the values nor how they map to bounds).  For each
+ * batch row b of segment_ids (batch, seq_len) int32, writes ranker_bounds
+ * (batch, 4) int32 = hl, hu, cl, cu where [hl, hu) is the smallest interval
+ * holding every position whose id is history_id and [cl, cu) likewise for
+ * candidate_id; an id that does not occur gives [0, 0).  For contiguous runs
+ * (the page's layout) that is exactly the run.  Both pointers are device
+ * memory, 4-byte aligned.  ATTN_ERR_PARAM if the two ids are equal. */
+attn_status attn_ranker_bounds(const int32_t* segment_ids, int32_t batch, int32_t seq_len,
+                               int32_t history_id, int32_t candidate_id, int32_t* ranker_bounds,
+                               void* stream);
 
 /* dK and dV (triton_kernels.py page, make_triton_backward_kernel_dkv), each
  * summed over the Hq/Hkv query heads of a key/value head inside one

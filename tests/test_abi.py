@@ -87,7 +87,18 @@ def test_null_and_misaligned_pointers_rejected_before_launch():
     cp = p.to_c()
     assert lib.attn_bwd_preprocess(ctypes.byref(cp), None, good, good, None) == -1
     assert lib.attn_bwd_dq(ctypes.byref(cp), good, good, good, None, None, None, good, good, good,
-                           good, good + 4, None) == -5
+                           good, good + 4, None, None) == -5
+    assert lib.attn_bwd_dq(ctypes.byref(cp), good, good, good, None, None, None, good, good, good,
+                           good, good, good + 2, None) == -5     # dtemp_h 4-byte aligned
+    assert "dtemp_h" in lib.attn_last_error().decode()
+    assert lib.attn_reduce_heads(ctypes.byref(cp), None, good, None) == -1
+    assert lib.attn_reduce_heads(ctypes.byref(cp), good, good + 1, None) == -5
+    assert lib.attn_reduce_heads(None, good, good, None) == -1
+    assert lib.attn_ranker_bounds(good, 2, 64, 3, 3, good, None) == -6   # ids must differ
+    assert lib.attn_ranker_bounds(good, 0, 64, 3, 4, good, None) == -2
+    assert lib.attn_ranker_bounds(good, 2, 0, 3, 4, good, None) == -2
+    assert lib.attn_ranker_bounds(None, 2, 64, 3, 4, good, None) == -1
+    assert lib.attn_ranker_bounds(good, 2, 64, 3, 4, good + 2, None) == -5
     assert lib.attn_bwd_dkv(ctypes.byref(cp), good, good, good, None, None, None, good, good, good,
                             good, good, None, None) == -1
     assert lib.attn_fwd(None, *ptrs, None) == -1

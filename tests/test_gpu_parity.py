@@ -36,11 +36,12 @@ def host_inputs(inp):
                 rb=to_i32(inp["ranker_bounds"]))
 
 
-def run_gpu(w: Workload, inp, precise=True):
+def run_gpu(w: Workload, inp, precise=True, dtemp=False):
     p = ba.params_for(w, precise)
     dev = {k: (v.cuda() if v is not None else None) for k, v in inp.items()}
     res = ba.attention_forward_backward(p, dev["q"], dev["k"], dev["v"], dev["do"],
-                                        dev["temperature"], dev["segment_ids"], dev["ranker_bounds"])
+                                        dev["temperature"], dev["segment_ids"], dev["ranker_bounds"],
+                                        dtemp=dtemp)
     torch.cuda.synchronize()
     return {k: v.cpu().double().numpy() for k, v in res.items()}
 
@@ -63,6 +64,20 @@ def check_tensor(name, got, ref, dtype):
         assert ma <= 3e-2, f"{name}: max-abs {ma:.3e} > 3e-2"
 
 
+def check_dtemp(got, ref, dtype):
+    """Temperature gradient: the gradient bars of its dtype, with max-abs taken
+    relative to the largest |dtemp| (its scale is set by the cap value, not 1)."""
+    assert got.shape == ref.shape and np.all(np.isfinite(got))
+    r = rel_l2(got, ref)
+    scale = max(1.0, float(np.abs(ref).max()))
+    ma = float(np.abs(got - ref).max()) / scale
+    say(f"  dtemp: rel-L2 {r:.2e} max-abs/scale {ma:.2e} (scale {scale:.2e})")
+    if dtype == "f32":
+        assert r <= 1e-5
+    else:
+        assert r <= 8e-3 and ma <= 3e-2
+
+
 def check_ml(got_m, got_l, ref_m, ref_l, dtype):
     empty = ~np.isfinite(ref_m)
     assert np.array_equal(~np.isfinite(got_m), empty), "m: empty rows differ"
@@ -80,10 +95,15 @@ def check_ml(got_m, got_l, ref_m, ref_l, dtype):
         assert dm <= 1e-3 and dl <= 1e-3
 
 
-def compare_full(w: Workload, precise=True, groups=None):
-    say(f"[parity] {w.name} B{w.B} Hq{w.Hq} Hkv{w.Hkv} L{w.L} D{w.D} {w.dtype} precise={precise}")
+def compare_full(w: Workload, precise=True, groups=None, dtemp=False):
+    say(f"[parity] {w.name} B{w.B} Hq{w.Hq} Hkv{w.Hkv} L{w.L} D{w.D} {w.dtype} precise={precise}"
+        f"{' dtemp' if dtemp else ''}")
     inp = make_inputs(w)
-    got = run_gpu(w, inp, precise)
+    got = run_gpu(w, inp, precise, dtemp=dtemp)
+    if dtemp:
+        # the dQ kernel variant that also sums dtemp gives the same dQ, bit for bit
+        plain = run_gpu(w, inp, precise)
+        assert np.array_equal(plain["dq"], got["dq"])
     h = host_inputs(inp)
     ref = backward(h["q"], h["k"], h["v"], h["do"], oracle_params(w), h["temp"], h["seg"], h["rb"],
                    groups=groups)
@@ -106,6 +126,10 @@ def compare_full(w: Workload, precise=True, groups=None):
     r = rel_l2(sel_d(got["delta"]), sel_d(ref["delta"]))
     say(f"  delta: rel-L2 {r:.2e}")
     assert r <= (1e-5 if w.dtype == "f32" else 8e-3)
+    if dtemp:
+        bs = sorted({b for b, _ in groups})
+        assert len(groups) == w.B * w.Hkv, "dtemp needs every group"
+        check_dtemp(got["dtemp"][bs], ref["dtemp"][bs], w.dtype)
     return got
 
 
@@ -130,6 +154,12 @@ def test_workload_reduced(cid):
 @pytest.mark.parametrize("cid", [4, 5])
 def test_workload_reduced_single_bf16_ds(cid):
     compare_full(REDUCED[cid], precise=False)
+
+
+@pytest.mark.parametrize("cid,precise", [(1, True), (2, True), (3, True), (4, True), (5, True),
+                                         (5, False)])
+def test_temperature_gradient_reduced(cid, precise):
+    compare_full(REDUCED[cid], precise=precise, dtemp=True)
 
 
 # ---------------------------------------------------------------------------
@@ -202,6 +232,25 @@ def test_full_workload_5_sampled(precise):
     keys = np.sort(rng.choice(np.arange(L - 4096, L), 32, replace=False))
     # causal: only rows >= the smallest sampled key can see the sampled keys
     sampled_checks(w, rows_by_head, keys, np.arange(keys.min(), L), 0, 0, precise)
+
+
+def test_full_workload_5_temperature_gradient_sampled():
+    """dtemp at the full long-context size (the launch configuration the
+    benchmark times, with the extra accumulation), on sampled rows summed over
+    all eight heads by the oracle."""
+    w = WORKLOADS[5]
+    rng = np.random.default_rng(2)
+    rows = np.sort(np.concatenate([rng.choice(w.L, 24, replace=False), [0, w.L - 1]]))
+    say(f"[parity-sampled] {w.name} dtemp rows {len(rows)}")
+    inp = make_inputs(w)
+    got = run_gpu(w, inp, precise=False, dtemp=True)
+    h = host_inputs(inp)
+    p = oracle_params(w)
+    ref = sum(dq_rows(h["q"], h["k"], h["v"], h["do"], p, 0, hq, rows, h["temp"], h["seg"],
+                      h["rb"])["dtemp_h"] for hq in range(w.Hq))
+    check_dtemp(got["dtemp"][0, rows], ref, w.dtype)
+    # the per-head shares add up to the reduced gradient
+    assert np.allclose(got["dtemp_h"].sum(axis=1), got["dtemp"], rtol=1e-6, atol=1e-6)
 
 
 # ---------------------------------------------------------------------------
@@ -335,3 +384,65 @@ def test_deterministic():
     b = run_gpu(w, inp)
     for n in a:
         assert np.array_equal(a[n], b[n], equal_nan=True), n
+
+
+# ---------------------------------------------------------------------------
+# Ranker bounds derived on the device from segment ids
+# ---------------------------------------------------------------------------
+
+def test_ranker_bounds_from_segment_ids_bit_exact():
+    from oracle import ranker_bounds_from_segments
+    HID, CID = 1 << 20, -7
+    rng = np.random.default_rng(5)
+    cases = []
+    for L in (1, 2, 255, 256, 257, 5000, 70001):
+        B = int(rng.integers(1, 6))
+        seg = rng.integers(0, 4, size=(B, L)).astype(np.int32)     # scattered ids
+        cases.append(seg)
+        runs = np.zeros((B, L), dtype=np.int32)                     # contiguous runs
+        for b in range(B):
+            h = int(rng.integers(0, L + 1))
+            c = int(rng.integers(h, L + 1))
+            runs[b, :h] = HID
+            runs[b, h:c] = CID
+        cases.append(runs)
+    edge = np.zeros((4, 9), dtype=np.int32)
+    edge[1, :] = HID                 # history only
+    edge[2, 0] = CID                 # one candidate at the start
+    edge[3, 8] = HID                 # one history position at the end
+    cases.append(edge)
+    for seg in cases:
+        seg = seg.copy()
+        seg[seg == 1] = HID
+        seg[seg == 2] = CID
+        ref = ranker_bounds_from_segments(seg, HID, CID)
+        got = ba.attn_ranker_bounds(torch.from_numpy(seg).cuda(), HID, CID)
+        torch.cuda.synchronize()
+        assert np.array_equal(got.cpu().numpy(), ref), (seg.shape, got.cpu().numpy(), ref)
+    say(f"  ranker bounds: {len(cases)} layouts bit-exact")
+
+
+def test_ranker_from_segment_ids_end_to_end():
+    """The ranker workload's layout (history [0, h), candidates [h, L)) written as
+    segment ids; bounds derived on the device drive the same attention, bit
+    for bit, as the workload's own bounds."""
+    HID, CID = 11, 12
+    w = REDUCED[4]
+    inp = make_inputs(w)
+    rb = inp["ranker_bounds"].numpy()
+    seg = np.zeros((w.B, w.L), dtype=np.int32)
+    for b in range(w.B):
+        seg[b, rb[b, 0]:rb[b, 1]] = HID
+        seg[b, rb[b, 2]:rb[b, 3]] = CID
+    dev_rb = ba.attn_ranker_bounds(torch.from_numpy(seg).cuda(), HID, CID)
+    torch.cuda.synchronize()
+    assert np.array_equal(dev_rb.cpu().numpy(), rb)
+    p = ba.params_for(w, True)
+    d = {k: (v.cuda() if v is not None else None) for k, v in inp.items()}
+    a = ba.attention_forward_backward(p, d["q"], d["k"], d["v"], d["do"], d["temperature"], None,
+                                      d["ranker_bounds"])
+    b_ = ba.attention_forward_backward(p, d["q"], d["k"], d["v"], d["do"], d["temperature"], None,
+                                       dev_rb)
+    torch.cuda.synchronize()
+    for n in ("o", "m", "l", "dq", "dk", "dv"):
+        assert torch.equal(a[n], b_[n]), n
