@@ -31,6 +31,9 @@ attn_status check_params(const attn_params* p) {
     return fail(ATTN_ERR_SHAPE, "seq_len exceeds ATTN_MAX_SEQ_LEN");
   if ((long long)p->batch * p->q_heads * p->seq_len > (1LL << 36))
     return fail(ATTN_ERR_SHAPE, "batch * q_heads * seq_len too large");
+  // tile loads address a tile as base + 32-bit byte offset (rows * Hq * D * 2)
+  if ((long long)p->q_heads * p->head_dim > (1LL << 22))
+    return fail(ATTN_ERR_SHAPE, "q_heads * head_dim exceeds 2^22");
   if (p->dtype != ATTN_F32 && p->dtype != ATTN_BF16)
     return fail(ATTN_ERR_DTYPE, "dtype must be ATTN_F32 or ATTN_BF16");
   if (p->head_dim != 64 && p->head_dim != 128)

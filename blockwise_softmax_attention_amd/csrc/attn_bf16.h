@@ -32,6 +32,8 @@
 
 namespace attn {
 
+__device__ __forceinline__ uint32_t imin_u(uint32_t a, uint32_t b) { return a < b ? a : b; }
+
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
@@ -39,10 +41,21 @@ __device__ __forceinline__ uint32_t lds_offset(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
 }
 
-// One 16-byte direct load per lane into LDS[m0 + 16 * lane]; m0 must be uniform.
-__device__ __forceinline__ void dma16(const void* gptr, uint32_t m0) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "s"(m0)
+// One 16-byte direct load per lane into LDS[m0 + 16 * lane] from the address
+// sbase + voff: sbase wave-uniform (scalar registers), voff a per-lane 32-bit
+// byte offset, so the address costs no 64-bit vector arithmetic; m0 uniform.
+__device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t m0) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(m0)
                : "memory", "m0");
+}
+
+// A pointer the caller knows to be the same on every lane, moved to scalar
+// registers.
+__device__ __forceinline__ const void* uniform_ptr(const void* p) {
+  const uint64_t u = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+  return (const void*)(uintptr_t)(((uint64_t)hi << 32) | lo);
 }
 
 template <int N>
@@ -79,55 +92,45 @@ struct BTile {
     return (2 * (lr & 3) + ((lr >> 2) & 1) + 8 * ((lr >> 3) & 1)) & (CPR - 1);
   }
 
-  // Issue this wave's share of the loads of one tile.  Load n = wave + NW i
+  // Per-lane part of every load address, computed once: load n = wave + NW i
   // fills LDS rows 4n .. 4n+3 (for 256-byte rows); with that interleaving a
-  // lane's row inside each 16-row group and its chunk are the same for all of
-  // its loads, so each address is one per-lane base plus a uniform offset.
-  // gbase: element (0, 0) of the tile; rows >= rows_valid read row
-  // rows_valid - 1 (only the last tile of a sequence needs the clamp).
-  __device__ __forceinline__ static void issue(uint32_t lds_base, const bf16* gbase, long row_stride,
-                                               int rows_valid, int lane, int wave) {
-    constexpr int LPR = RB / 16;              // lanes per row in one load
-    constexpr int RPI = 64 / LPR;             // rows per load
-    static_assert(RPI * NW <= 32 && 32 % (RPI * NW) == 0, "load pattern must tile 32-row blocks");
-    const int x = wave * RPI + lane / LPR;    // LDS row inside the group of RPI*NW rows
-    const int pos = lane % LPR;
-    const int c = pos ^ swz(x);
-    const int prow0 = pi32(x);                // row inside the group (pi keeps groups of 16)
-    const bf16* lane_base = gbase + (long)prow0 * row_stride + c * 8;
-    if (rows_valid >= ROWS) {
-#pragma unroll
-      for (int i = 0; i < PER_WAVE; ++i) {
-        const int n = wave + NW * i;
-        dma16(lane_base + (long)(i * RPI * NW) * row_stride,
-              (uint32_t)__builtin_amdgcn_readfirstlane(lds_base + n * 1024));
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < PER_WAVE; ++i) {
-        const int n = wave + NW * i;
-        int prow = i * RPI * NW + prow0;
-        prow = prow < rows_valid ? prow : rows_valid - 1;
-        dma16(gbase + (long)prow * row_stride + c * 8,
-              (uint32_t)__builtin_amdgcn_readfirstlane(lds_base + n * 1024));
-      }
-    }
+  // lane's row inside each group of RPI*NW rows and its chunk are the same for
+  // all of its loads, so its byte offset is off0 plus a uniform i * step.
+  struct Lane {
+    uint32_t off0;    // byte offset of this lane's 16 bytes in load 0
+    uint32_t cbyte;   // byte offset of its chunk inside a row
+  };
+  static constexpr int LPR = RB / 16;              // lanes per row in one load
+  static constexpr int RPI = 64 / LPR;             // rows per load
+  static_assert(RPI * NW <= 32 && 32 % (RPI * NW) == 0, "load pattern must tile 32-row blocks");
+
+  // rsb: global row stride in bytes.
+  __device__ __forceinline__ static Lane lane_of(uint32_t rsb, int lane, int wave) {
+    const int x = wave * RPI + lane / LPR;         // LDS row inside the group of RPI*NW rows
+    const int c = (lane % LPR) ^ swz(x);
+    Lane l;
+    l.cbyte = (uint32_t)c * 16u;
+    l.off0 = (uint32_t)pi32(x) * rsb + l.cbyte;    // pi keeps groups of 16 rows
+    return l;
   }
 
-  // Load i (0 <= i < PER_WAVE) of this wave's share of one tile, the same
-  // instruction issue() would send; lets a kernel spread its loads over its
-  // compute instead of sending them in one burst.
-  __device__ __forceinline__ static void issue_one(uint32_t lds_base, const bf16* gbase, long row_stride,
-                                                   int rows_valid, int lane, int wave, int i) {
-    constexpr int LPR = RB / 16;
-    constexpr int RPI = 64 / LPR;
-    const int x = wave * RPI + lane / LPR;
-    const int pos = lane % LPR;
-    const int c = pos ^ swz(x);
+  // Load i (0 <= i < PER_WAVE) of this wave's share of one tile.  gbase:
+  // element (0, 0) of the tile (wave-uniform); rows >= rows_valid read row
+  // rows_valid - 1 (finite data the masks zero; only the last tile of a
+  // sequence has such rows).
+  __device__ __forceinline__ static void issue_one(uint32_t lds_base, const bf16* gbase, uint32_t rsb,
+                                                   int rows_valid, const Lane& ln, int wave, int i) {
     const int n = wave + NW * i;
-    const int prow = imin(i * RPI * NW + pi32(x), rows_valid - 1);
-    dma16(gbase + (long)prow * row_stride + c * 8,
-          (uint32_t)__builtin_amdgcn_readfirstlane(lds_base + n * 1024));
+    const uint32_t lim = (uint32_t)(rows_valid - 1) * rsb + ln.cbyte;
+    const uint32_t off = imin_u(ln.off0 + (uint32_t)(i * RPI * NW) * rsb, lim);
+    dma16(uniform_ptr(gbase), off, (uint32_t)__builtin_amdgcn_readfirstlane(lds_base + n * 1024));
+  }
+
+  // All of this wave's loads of one tile.
+  __device__ __forceinline__ static void issue(uint32_t lds_base, const bf16* gbase, uint32_t rsb,
+                                               int rows_valid, const Lane& ln, int wave) {
+#pragma unroll
+    for (int i = 0; i < PER_WAVE; ++i) issue_one(lds_base, gbase, rsb, rows_valid, ln, wave, i);
   }
 
   // A operand, reduction over D: rows blk*32 + lane%32 (LDS order), step t.

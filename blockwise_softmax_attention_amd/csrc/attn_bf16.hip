@@ -99,11 +99,12 @@ __device__ __forceinline__ RowItem decode_row_item(const KArgs& a, int item, int
 // ---------------------------------------------------------------------------
 // Forward
 // ---------------------------------------------------------------------------
-template <bool MASKED, bool SEG, int CAP, int NKB, int NDB>
-__device__ __forceinline__ void fwd_softmax(f32x16 (&s)[NKB], f32x16 (&o)[NDB], float& m_base,
-                                            float& m_true, float& l_run, const KArgs& a,
-                                            const RowC& rc, const QMask& qm, int k0, int hh,
-                                            const int* sseg, int seg_q) {
+// Logits of one tile in the log2 domain (lane = query): s becomes
+// fma(f(x), Kf, C2) (masked pairs -inf); returns this lane's maximum.
+template <bool MASKED, bool SEG, int CAP, int NKB>
+__device__ __forceinline__ float fwd_logits(f32x16 (&s)[NKB], const KArgs& a, const RowC& rc,
+                                            const QMask& qm, int k0, int hh, const int* sseg,
+                                            int seg_q) {
   using CapF = Cap<CAP, false>;
   float mx = ATTN_NEG_INF;
 #pragma unroll
@@ -122,6 +123,16 @@ __device__ __forceinline__ void fwd_softmax(f32x16 (&s)[NKB], f32x16 (&o)[NDB], 
       mx = fmaxf(mx, w);
     }
   }
+  return mx;
+}
+
+// Online-softmax update of one tile (every tile class shares it): the
+// running base m_base moves only when the tile's maximum exceeds it by more
+// than RESCALE_TAU (then O and l are rescaled); m_true tracks the exact
+// maximum; s becomes P = exp2(w - m_base) and its row sum is added to l.
+template <int NKB, int NDB>
+__device__ __forceinline__ void fwd_update(f32x16 (&s)[NKB], f32x16 (&o)[NDB], float mx, float& m_base,
+                                           float& m_true, float& l_run) {
   mx = half_max(mx);
   m_true = fmaxf(m_true, mx);
   if (__ballot(mx > m_base + RESCALE_TAU) != 0) {
@@ -134,15 +145,18 @@ __device__ __forceinline__ void fwd_softmax(f32x16 (&s)[NKB], f32x16 (&o)[NDB], 
     m_base = m_new;
   }
   const float base = (m_base == ATTN_NEG_INF) ? 0.f : m_base;
+  // four partial sums: a single running sum would be one dependent chain
+  float ls[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const float p = fast_exp2(s[kb][r] - base);
-      l_run += p;
+      ls[r & 3] += p;
       s[kb][r] = p;
     }
   }
+  l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
 }
 
 template <int D, int CAP, bool PRECISE>
@@ -167,6 +181,8 @@ __global__ __launch_bounds__(NTHREADS, ATTN_FWD_WAVES_PER_SIMD) void fwd_bf16_ke
   const bool row_ok = qrow < L;
 
   const long q_rs = (long)a.Hq * D, kv_rs = (long)a.Hkv * D;
+  const uint32_t kv_rsb = (uint32_t)(kv_rs * sizeof(bf16));   // K, V row stride in bytes
+  const typename KT::Lane kln = KT::lane_of(kv_rsb, lane, wave);
   const bf16* Qb = (const bf16*)a.q + ((long)b * L * a.Hq + it.hq) * D;
   const bf16* Kb = (const bf16*)a.k + ((long)b * L * a.Hkv + it.hkv) * D;
   const bf16* Vb = (const bf16*)a.v + ((long)b * L * a.Hkv + it.hkv) * D;
@@ -197,15 +213,15 @@ __global__ __launch_bounds__(NTHREADS, ATTN_FWD_WAVES_PER_SIMD) void fwd_bf16_ke
   };
   int pseg = -1;
   auto issue = [&](int j, int st) {
-    KT::issue(lds_offset(sK[st]), Kb + (long)(j * BN) * kv_rs, kv_rs, L - j * BN, lane, wave);
-    KT::issue(lds_offset(sV[st]), Vb + (long)(j * BN) * kv_rs, kv_rs, L - j * BN, lane, wave);
+    KT::issue(lds_offset(sK[st]), Kb + (long)(j * BN) * kv_rs, kv_rsb, L - j * BN, kln, wave);
+    KT::issue(lds_offset(sV[st]), Vb + (long)(j * BN) * kv_rs, kv_rsb, L - j * BN, kln, wave);
   };
   // load i of this wave's 2 PER_WAVE loads of the K and V tiles of key tile j
   auto issue_one = [&](int j, int st, int i) {
     if (i < KT::PER_WAVE)
-      KT::issue_one(lds_offset(sK[st]), Kb + (long)(j * BN) * kv_rs, kv_rs, L - j * BN, lane, wave, i);
+      KT::issue_one(lds_offset(sK[st]), Kb + (long)(j * BN) * kv_rs, kv_rsb, L - j * BN, kln, wave, i);
     else
-      KT::issue_one(lds_offset(sV[st]), Vb + (long)(j * BN) * kv_rs, kv_rs, L - j * BN, lane, wave,
+      KT::issue_one(lds_offset(sV[st]), Vb + (long)(j * BN) * kv_rs, kv_rsb, L - j * BN, kln, wave,
                     i - KT::PER_WAVE);
   };
   constexpr int NDMA = 2 * KT::PER_WAVE;
@@ -269,14 +285,15 @@ __global__ __launch_bounds__(NTHREADS, ATTN_FWD_WAVES_PER_SIMD) void fwd_bf16_ke
     // the tile class is the same on every lane; readfirstlane lets the compiler
     // branch on it instead of running every variant under an exec mask
     const int tcls = __builtin_amdgcn_readfirstlane(tile_class(it.qw0, it.qw0 + 32, k0, k0 + BN, ms));
+    float mx;
     if (tcls == TILE_FULL) {
-      fwd_softmax<false, false, CAP>(sacc, oacc, m_base, m_true, l_run, a, rc, qm, k0, hh, nullptr, 0);
+      mx = fwd_logits<false, false, CAP>(sacc, a, rc, qm, k0, hh, nullptr, 0);
     } else if (!seg_any) {
-      fwd_softmax<true, false, CAP>(sacc, oacc, m_base, m_true, l_run, a, rc, qm, k0, hh, nullptr, 0);
+      mx = fwd_logits<true, false, CAP>(sacc, a, rc, qm, k0, hh, nullptr, 0);
     } else {
-      fwd_softmax<true, true, CAP>(sacc, oacc, m_base, m_true, l_run, a, rc, qm, k0, hh, sSeg[st],
-                                   seg_q);
+      mx = fwd_logits<true, true, CAP>(sacc, a, rc, qm, k0, hh, sSeg[st], seg_q);
     }
+    fwd_update(sacc, oacc, mx, m_base, m_true, l_run);
 #pragma unroll
     for (int t = 0; t < BN / 16; ++t) {
       // With PRECISE, P enters as hi + lo bf16 parts so that O (and the delta
@@ -377,6 +394,8 @@ __global__ __launch_bounds__(NTHREADS, 2) void dq_bf16_kernel(KArgs a) {
   const bool row_ok = qrow < L;
 
   const long q_rs = (long)a.Hq * D, kv_rs = (long)a.Hkv * D;
+  const uint32_t kv_rsb = (uint32_t)(kv_rs * sizeof(bf16));   // K, V row stride in bytes
+  const typename KT::Lane kln = KT::lane_of(kv_rsb, lane, wave);
   const bf16* Qb = (const bf16*)a.q + ((long)b * L * a.Hq + it.hq) * D;
   const bf16* dOb = (const bf16*)a.dout + ((long)b * L * a.Hq + it.hq) * D;
   const bf16* Kb = (const bf16*)a.k + ((long)b * L * a.Hkv + it.hkv) * D;
@@ -415,15 +434,15 @@ __global__ __launch_bounds__(NTHREADS, 2) void dq_bf16_kernel(KArgs a) {
   };
   int pseg = -1;
   auto issue = [&](int j, int st) {
-    KT::issue(lds_offset(sK[st]), Kb + (long)(j * BN) * kv_rs, kv_rs, L - j * BN, lane, wave);
-    KT::issue(lds_offset(sV[st]), Vb + (long)(j * BN) * kv_rs, kv_rs, L - j * BN, lane, wave);
+    KT::issue(lds_offset(sK[st]), Kb + (long)(j * BN) * kv_rs, kv_rsb, L - j * BN, kln, wave);
+    KT::issue(lds_offset(sV[st]), Vb + (long)(j * BN) * kv_rs, kv_rsb, L - j * BN, kln, wave);
   };
   // load i of this wave's 2 PER_WAVE loads of the K and V tiles of key tile j
   auto issue_one = [&](int j, int st, int i) {
     if (i < KT::PER_WAVE)
-      KT::issue_one(lds_offset(sK[st]), Kb + (long)(j * BN) * kv_rs, kv_rs, L - j * BN, lane, wave, i);
+      KT::issue_one(lds_offset(sK[st]), Kb + (long)(j * BN) * kv_rs, kv_rsb, L - j * BN, kln, wave, i);
     else
-      KT::issue_one(lds_offset(sV[st]), Vb + (long)(j * BN) * kv_rs, kv_rs, L - j * BN, lane, wave,
+      KT::issue_one(lds_offset(sV[st]), Vb + (long)(j * BN) * kv_rs, kv_rsb, L - j * BN, kln, wave,
                     i - KT::PER_WAVE);
   };
   constexpr int NDMA = 2 * KT::PER_WAVE;
@@ -604,6 +623,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void dkv_bf16_kernel(KArgs a) {
   const bool key_ok = krow < L;
 
   const long q_rs = (long)a.Hq * D, kv_rs = (long)a.Hkv * D;
+  const uint32_t q_rsb = (uint32_t)(q_rs * sizeof(bf16));     // Q, dO row stride in bytes
+  const typename QT::Lane qln = QT::lane_of(q_rsb, lane, wave);
   const bf16* Kb = (const bf16*)a.k + ((long)b * L * a.Hkv + hkv) * D;
   const bf16* Vb = (const bf16*)a.v + ((long)b * L * a.Hkv + hkv) * D;
 
@@ -691,10 +712,10 @@ __global__ __launch_bounds__(NTHREADS, 1) void dkv_bf16_kernel(KArgs a) {
   auto issue = [&](int g, int t, int stg) {
     const int hq = hkv * G + g;
     const int qb0 = t * BQ;
-    QT::issue(lds_offset(sQ[stg]), (const bf16*)a.q + (((long)b * L + qb0) * a.Hq + hq) * D, q_rs,
-              L - qb0, lane, wave);
-    QT::issue(lds_offset(sO[stg]), (const bf16*)a.dout + (((long)b * L + qb0) * a.Hq + hq) * D, q_rs,
-              L - qb0, lane, wave);
+    QT::issue(lds_offset(sQ[stg]), (const bf16*)a.q + (((long)b * L + qb0) * a.Hq + hq) * D, q_rsb,
+              L - qb0, qln, wave);
+    QT::issue(lds_offset(sO[stg]), (const bf16*)a.dout + (((long)b * L + qb0) * a.Hq + hq) * D, q_rsb,
+              L - qb0, qln, wave);
   };
   // Load i of the 2 PER_WAVE loads of this wave for the Q and dO tiles of
   // step (g, t): the first PER_WAVE go to Q, the rest to dO.
@@ -702,11 +723,11 @@ __global__ __launch_bounds__(NTHREADS, 1) void dkv_bf16_kernel(KArgs a) {
     const int hq = hkv * G + g;
     const int qb0 = t * BQ;
     if (i < QT::PER_WAVE) {
-      QT::issue_one(lds_offset(sQ[stg]), (const bf16*)a.q + (((long)b * L + qb0) * a.Hq + hq) * D, q_rs,
-                    L - qb0, lane, wave, i);
+      QT::issue_one(lds_offset(sQ[stg]), (const bf16*)a.q + (((long)b * L + qb0) * a.Hq + hq) * D, q_rsb,
+                    L - qb0, qln, wave, i);
     } else {
-      QT::issue_one(lds_offset(sO[stg]), (const bf16*)a.dout + (((long)b * L + qb0) * a.Hq + hq) * D, q_rs,
-                    L - qb0, lane, wave, i - QT::PER_WAVE);
+      QT::issue_one(lds_offset(sO[stg]), (const bf16*)a.dout + (((long)b * L + qb0) * a.Hq + hq) * D, q_rsb,
+                    L - qb0, qln, wave, i - QT::PER_WAVE);
     }
   };
   constexpr int NDMA = 2 * QT::PER_WAVE;

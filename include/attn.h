@@ -62,7 +62,8 @@ extern "C" {
 typedef enum {
   ATTN_OK = 0,
   ATTN_ERR_NULL_PTR = -1,    /* a required pointer is NULL */
-  ATTN_ERR_SHAPE = -2,       /* a size is < 1 (L, B, heads) or too large */
+  ATTN_ERR_SHAPE = -2,       /* a size is < 1 (L, B, heads) or too large (L, B*Hq*L > 2^36,
+                                Hq*D > 2^22) */
   ATTN_ERR_DTYPE = -3,       /* dtype is neither ATTN_F32 nor ATTN_BF16 */
   ATTN_ERR_UNSUPPORTED = -4, /* head_dim not 64 or 128, or Hq not a multiple of Hkv */
   ATTN_ERR_ALIGN = -5,       /* a tensor pointer is not 16-byte aligned */
