@@ -758,71 +758,128 @@ __global__ __launch_bounds__(NTHREADS, 1) void dkv_bf16_kernel(KArgs a) {
     const int q0 = tc * BQ;
     const char* Qt = sQ[stg];
     const char* Ot = sO[stg];
-    f32x16 sacc[NQB], pacc[NQB];
-#pragma unroll
-    for (int qb = 0; qb < NQB; ++qb) sacc[qb] = pacc[qb] = f32x16{};
-    // Software pipeline over the reduction steps: the LDS fragments of step
-    // t + 1 are requested before the MFMAs of step t, and a scheduling fence
-    // keeps the compiler from sinking them next to their use (which would
-    // expose one LDS latency per MFMA).
-    bf16x8 fq[2][NQB], fo[2][NQB];
-#pragma unroll
-    for (int qb = 0; qb < NQB; ++qb) {
-      fq[0][qb] = QT::row_frag(Qt, qb, 0, lane);
-      fo[0][qb] = QT::row_frag(Ot, qb, 0, lane);
-    }
-#pragma unroll
-    for (int t = 0; t < NT16; ++t) {
-      const int cur = t & 1;
-      if (t + 1 < NT16) {
-#pragma unroll
-        for (int qb = 0; qb < NQB; ++qb) {
-          fq[cur ^ 1][qb] = QT::row_frag(Qt, qb, t + 1, lane);
-          fo[cur ^ 1][qb] = QT::row_frag(Ot, qb, t + 1, lane);
-        }
-      }
-#pragma unroll
-      for (int qb = 0; qb < NQB; ++qb) {
-        sacc[qb] = Elem<bf16>::mfma(fq[cur][qb], kf[t], sacc[qb]);
-        pacc[qb] = Elem<bf16>::mfma(fo[cur][qb], vf[t], pacc[qb]);
-      }
-      if (t + 1 < NT16) __builtin_amdgcn_sched_group_barrier(0x100, 2 * NQB, 0);   // LDS reads
-      __builtin_amdgcn_sched_group_barrier(0x008, 2 * NQB, 0);                      // then MFMAs
-      // the next step's tile loads, spread over the reduction steps: sent in
-      // one burst they keep the wave waiting at issue
-#pragma unroll
-      for (int i = t * NDMA / NT16; i < (t + 1) * NDMA / NT16; ++i) issue_one(gn, tn, stg ^ 1, i);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    fetch_consts(gn, tn);
+    static_assert(NQB == 2, "the dK/dV step schedules two 32-query blocks");
     // the tile class is the same on every lane; readfirstlane lets the compiler
     // branch on it instead of running every variant under an exec mask
     const int tcls = __builtin_amdgcn_readfirstlane(tile_class(q0, q0 + BQ, kw0, kw0 + 32, ms));
-    if (tcls == TILE_FULL) {
-      dkv_elementwise<false, false, CAP>(sacc, pacc, a, sKf[stg], sC2[stg], sDl[stg], sR[stg], km, q0,
-                                         hh, nullptr, 0);
-    } else if (!seg_any) {
-      dkv_elementwise<true, false, CAP>(sacc, pacc, a, sKf[stg], sC2[stg], sDl[stg], sR[stg], km, q0,
-                                        hh, nullptr, 0);
-    } else {
-      dkv_elementwise<true, true, CAP>(sacc, pacc, a, sKf[stg], sC2[stg], sDl[stg], sR[stg], km, q0,
-                                       hh, sSeg[stg], seg_k);
-    }
-#pragma unroll
-    for (int t = 0; t < BQ / 16; ++t) {
-      const bf16x8 pb = Elem<bf16>::from_acc(sacc[t / 2], 8 * (t % 2));
-      bf16x8 hi, lo;
-      if (PRECISE) {
-        Elem<bf16>::split_acc(pacc[t / 2], 8 * (t % 2), hi, lo);
+    auto elementwise = [&](f32x16 (&sa)[1], f32x16 (&pa)[1], int qb) {
+      const int o = 32 * qb;
+      if (tcls == TILE_FULL) {
+        dkv_elementwise<false, false, CAP>(sa, pa, a, sKf[stg] + o, sC2[stg] + o, sDl[stg] + o,
+                                           sR[stg] + o, km, q0 + o, hh, nullptr, 0);
+      } else if (!seg_any) {
+        dkv_elementwise<true, false, CAP>(sa, pa, a, sKf[stg] + o, sC2[stg] + o, sDl[stg] + o,
+                                          sR[stg] + o, km, q0 + o, hh, nullptr, 0);
       } else {
-        hi = Elem<bf16>::from_acc(pacc[t / 2], 8 * (t % 2));
+        dkv_elementwise<true, true, CAP>(sa, pa, a, sKf[stg] + o, sC2[stg] + o, sDl[stg] + o,
+                                         sR[stg] + o, km, q0 + o, hh, sSeg[stg] + o, seg_k);
       }
+    };
+    // bf16 operands of dV / dK for one block: P (pb) and dS (hi [+ lo]) per
+    // 16-query half h
+    auto pack = [&](const f32x16& sa, const f32x16& pa, bf16x8 (&pb)[2], bf16x8 (&hi)[2],
+                    bf16x8 (&lo)[2]) {
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        dvacc[db] = Elem<bf16>::mfma(QT::tr_frag(Ot, db, t, lane), pb, dvacc[db]);
-        const bf16x8 qa = QT::tr_frag(Qt, db, t, lane);
-        dkacc[db] = Elem<bf16>::mfma(qa, hi, dkacc[db]);
-        if (PRECISE) dkacc[db] = Elem<bf16>::mfma(qa, lo, dkacc[db]);
+      for (int h = 0; h < 2; ++h) {
+        pb[h] = Elem<bf16>::from_acc(sa, 8 * h);
+        if (PRECISE) {
+          Elem<bf16>::split_acc(pa, 8 * h, hi[h], lo[h]);
+        } else {
+          hi[h] = Elem<bf16>::from_acc(pa, 8 * h);
+        }
+      }
+    };
+    // dV / dK unit u = (h, db) of block qb: 2 MFMAs (3 with PRECISE)
+    auto dvdk_unit = [&](int qb, int u, const bf16x8 (&pb)[2], const bf16x8 (&hi)[2],
+                         const bf16x8 (&lo)[2], const bf16x8& oa, const bf16x8& qa) {
+      const int h = u / NDB, db = u % NDB;
+      (void)qb;
+      dvacc[db] = Elem<bf16>::mfma(oa, pb[h], dvacc[db]);
+      dkacc[db] = Elem<bf16>::mfma(qa, hi[h], dkacc[db]);
+      if (PRECISE) dkacc[db] = Elem<bf16>::mfma(qa, lo[h], dkacc[db]);
+    };
+    auto tr_pair = [&](int qb, int u, bf16x8& oa, bf16x8& qa) {
+      const int h = u / NDB, db = u % NDB, tt = 2 * qb + h;
+      oa = QT::tr_frag(Ot, db, tt, lane);
+      qa = QT::tr_frag(Qt, db, tt, lane);
+    };
+    constexpr int NU = 2 * NDB;   // dV / dK units per block
+    static_assert(NU == NT16 || NU * 2 == NT16, "units per reduction step");
+    constexpr int UPT = NU / NT16 > 0 ? NU / NT16 : 1;   // units per S/dP reduction step
+    constexpr int TPU = NT16 / NU > 0 ? NT16 / NU : 1;   // reduction steps per unit
+
+    // Block 0: S / dP (two MFMA chains, LDS fragments one step ahead, this
+    // step's tile loads spread over the first half), then its element work.
+    f32x16 s0[1] = {f32x16{}}, p0[1] = {f32x16{}};
+    {
+      bf16x8 fq[2], fo[2];
+      fq[0] = QT::row_frag(Qt, 0, 0, lane);
+      fo[0] = QT::row_frag(Ot, 0, 0, lane);
+#pragma unroll
+      for (int t = 0; t < NT16; ++t) {
+        const int cur = t & 1;
+        if (t + 1 < NT16) {
+          fq[cur ^ 1] = QT::row_frag(Qt, 0, t + 1, lane);
+          fo[cur ^ 1] = QT::row_frag(Ot, 0, t + 1, lane);
+        }
+        s0[0] = Elem<bf16>::mfma(fq[cur], kf[t], s0[0]);
+        p0[0] = Elem<bf16>::mfma(fo[cur], vf[t], p0[0]);
+        if (t + 1 < NT16) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+#pragma unroll
+        for (int i = t * NDMA / (2 * NT16); i < (t + 1) * NDMA / (2 * NT16); ++i)
+          issue_one(gn, tn, stg ^ 1, i);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    fetch_consts(gn, tn);
+    elementwise(s0, p0, 0);
+    bf16x8 pb0[2], hi0[2], lo0[2];
+    pack(s0[0], p0[0], pb0, hi0, lo0);
+    // Block 1's S / dP with block 0's dV / dK between them: ~10 independent
+    // MFMA chains in flight, and only one block's S / dP accumulators live.
+    f32x16 s1[1] = {f32x16{}}, p1[1] = {f32x16{}};
+    {
+      bf16x8 fq[2], fo[2], ta[2], tb[2];
+      fq[0] = QT::row_frag(Qt, 1, 0, lane);
+      fo[0] = QT::row_frag(Ot, 1, 0, lane);
+      tr_pair(0, 0, ta[0], tb[0]);
+#pragma unroll
+      for (int t = 0; t < NT16; ++t) {
+        const int cur = t & 1;
+        if (t + 1 < NT16) {
+          fq[cur ^ 1] = QT::row_frag(Qt, 1, t + 1, lane);
+          fo[cur ^ 1] = QT::row_frag(Ot, 1, t + 1, lane);
+        }
+        s1[0] = Elem<bf16>::mfma(fq[cur], kf[t], s1[0]);
+        p1[0] = Elem<bf16>::mfma(fo[cur], vf[t], p1[0]);
+        if (t % TPU == 0) {
+#pragma unroll
+          for (int k = 0; k < UPT; ++k) {
+            const int u = (t / TPU) * UPT + k;
+            const int c = u & 1;
+            if (u + 1 < NU) tr_pair(0, u + 1, ta[c ^ 1], tb[c ^ 1]);
+            dvdk_unit(0, u, pb0, hi0, lo0, ta[c], tb[c]);
+          }
+        }
+#pragma unroll
+        for (int i = NDMA / 2 + t * NDMA / (2 * NT16); i < NDMA / 2 + (t + 1) * NDMA / (2 * NT16); ++i)
+          issue_one(gn, tn, stg ^ 1, i);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    elementwise(s1, p1, 1);
+    {
+      bf16x8 pb1[2], hi1[2], lo1[2];
+      pack(s1[0], p1[0], pb1, hi1, lo1);
+      bf16x8 ta[2], tb[2];
+      tr_pair(1, 0, ta[0], tb[0]);
+#pragma unroll
+      for (int u = 0; u < NU; ++u) {
+        const int c = u & 1;
+        if (u + 1 < NU) tr_pair(1, u + 1, ta[c ^ 1], tb[c ^ 1]);
+        dvdk_unit(1, u, pb1, hi1, lo1, ta[c], tb[c]);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
     if (more) store_consts(stg ^ 1);
