@@ -126,13 +126,41 @@ __device__ __forceinline__ float fwd_logits(f32x16 (&s)[NKB], const KArgs& a, co
   return mx;
 }
 
+// Sign of the logit's slope in the cap output f for the fast forms of
+// Cap<> (logit = f kmul t + kadd t): kmul < 0 only for the tanh form.
+template <int CAP> struct CapSlope {
+  static constexpr float value = (CAP == 1) ? -1.f : 1.f;
+};
+
+// Full tiles whose rows all have a slope Kf of the sign CapSlope (temperature
+// >= 0): s keeps the cap output f and the row maximum of the logits comes from
+// the extreme f (the logit fma(f, Kf, C2) is monotone in f, and so is its
+// rounding); the exponent later folds C2 - base into one fma.
+template <int CAP, int NKB>
+__device__ __forceinline__ float fwd_caps(f32x16 (&s)[NKB], const KArgs& a, const RowC& rc) {
+  using CapF = Cap<CAP, false>;
+  constexpr bool POS = CapSlope<CAP>::value > 0.f;
+  float ext = POS ? ATTN_NEG_INF : ATTN_POS_INF;
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float aux;
+      const float f = CapF::f(s[kb][r], a, aux);
+      s[kb][r] = f;
+      ext = POS ? fmaxf(ext, f) : fminf(ext, f);
+    }
+  }
+  return __builtin_fmaf(ext, rc.Kf, rc.C2);
+}
+
 // Online-softmax update of one tile (every tile class shares it): the
 // running base m_base moves only when the tile's maximum exceeds it by more
 // than RESCALE_TAU (then O and l are rescaled); m_true tracks the exact
-// maximum; s becomes P = exp2(w - m_base) and its row sum is added to l.
-template <int NKB, int NDB>
-__device__ __forceinline__ void fwd_update(f32x16 (&s)[NKB], f32x16 (&o)[NDB], float mx, float& m_base,
-                                           float& m_true, float& l_run) {
+// maximum.  Returns the base the exponents are taken against.
+template <int NDB>
+__device__ __forceinline__ float fwd_rescale(f32x16 (&o)[NDB], float mx, float& m_base, float& m_true,
+                                             float& l_run) {
   mx = half_max(mx);
   m_true = fmaxf(m_true, mx);
   if (__ballot(mx > m_base + RESCALE_TAU) != 0) {
@@ -144,14 +172,21 @@ __device__ __forceinline__ void fwd_update(f32x16 (&s)[NKB], f32x16 (&o)[NDB], f
     for (int i = 0; i < NDB; ++i) o[i] *= alpha;
     m_base = m_new;
   }
-  const float base = (m_base == ATTN_NEG_INF) ? 0.f : m_base;
+  return (m_base == ATTN_NEG_INF) ? 0.f : m_base;
+}
+
+// s becomes P = exp2(logit - base) and its row sum is added to l; FDOM: s
+// holds the cap output f (logit = fma(f, Kf, C2)), else the logit itself.
+template <bool FDOM, int NKB>
+__device__ __forceinline__ void fwd_exp(f32x16 (&s)[NKB], float base, const RowC& rc, float& l_run) {
+  const float c2b = rc.C2 - base;
   // four partial sums: a single running sum would be one dependent chain
   float ls[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const float p = fast_exp2(s[kb][r] - base);
+      const float p = FDOM ? fast_exp2(__builtin_fmaf(s[kb][r], rc.Kf, c2b)) : fast_exp2(s[kb][r] - base);
       ls[r & 3] += p;
       s[kb][r] = p;
     }
@@ -198,6 +233,10 @@ __global__ __launch_bounds__(NTHREADS, ATTN_FWD_WAVES_PER_SIMD) void fwd_bf16_ke
   for (int t = 0; t < NT16; ++t) qf[t] = global_frag<bf16>(Qb + (long)qrow * q_rs + 16 * t + 8 * hh, row_ok);
   const float tmp = (a.temp != nullptr && row_ok) ? a.temp[(long)b * L + qrow] : 1.f;
   const RowC rc = row_consts(a, tmp, 0.f);
+  // every row of the wave has a logit slope of the expected sign (temperature
+  // >= 0, not NaN): full tiles may then take the row maximum over f
+  const bool mono = __builtin_amdgcn_readfirstlane(
+                        (int)(__ballot(!(rc.Kf * CapSlope<CAP>::value >= 0.f)) == 0)) != 0;
   const int seg_q = (has_seg && row_ok) ? segb[qrow] : 0;
 
   int t_lo = 0, t_hi = 0;
@@ -286,14 +325,22 @@ __global__ __launch_bounds__(NTHREADS, ATTN_FWD_WAVES_PER_SIMD) void fwd_bf16_ke
     // branch on it instead of running every variant under an exec mask
     const int tcls = __builtin_amdgcn_readfirstlane(tile_class(it.qw0, it.qw0 + 32, k0, k0 + BN, ms));
     float mx;
-    if (tcls == TILE_FULL) {
+    const bool fdom = tcls == TILE_FULL && mono;
+    if (fdom) {
+      mx = fwd_caps<CAP>(sacc, a, rc);
+    } else if (tcls == TILE_FULL) {
       mx = fwd_logits<false, false, CAP>(sacc, a, rc, qm, k0, hh, nullptr, 0);
     } else if (!seg_any) {
       mx = fwd_logits<true, false, CAP>(sacc, a, rc, qm, k0, hh, nullptr, 0);
     } else {
       mx = fwd_logits<true, true, CAP>(sacc, a, rc, qm, k0, hh, sSeg[st], seg_q);
     }
-    fwd_update(sacc, oacc, mx, m_base, m_true, l_run);
+    const float base = fwd_rescale(oacc, mx, m_base, m_true, l_run);
+    if (fdom) {
+      fwd_exp<true>(sacc, base, rc, l_run);
+    } else {
+      fwd_exp<false>(sacc, base, rc, l_run);
+    }
 #pragma unroll
     for (int t = 0; t < BN / 16; ++t) {
       // With PRECISE, P enters as hi + lo bf16 parts so that O (and the delta

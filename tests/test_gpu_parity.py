@@ -360,6 +360,30 @@ def test_bf16_every_cap(D, cap):
                    z_loss_weight=0.01, temperature=(0.8, 1.2), sm_scale=1 / math.sqrt(D)))
 
 
+@pytest.mark.parametrize("cap", [("tanh", 5.0, 0.0, 0.0), ("alsc", 6.0, 3.0, 0.25)])
+def test_temperatures_of_any_sign(cap):
+    """Zero and negative temperatures (the forward's shortcut for full tiles
+    needs every row of a wave to have a non-negative one; others take the
+    general path), bf16, with the temperature gradient."""
+    method, c, al, be = cap
+    w = W(L=300, Hq=2, Hkv=1, D=128, cap_method=method, cap=c, alpha=al, beta=be, causal=True,
+          z_loss_weight=0.05)
+    inp = make_inputs(w)
+    tmp = torch.rand((1, w.L), generator=torch.Generator().manual_seed(3)) * 1.4 + 0.3
+    tmp[0, 40:70] = -tmp[0, 40:70]          # a run of negative rows
+    tmp[0, 130] = 0.0                       # a zero row
+    tmp[0, 200:232] = -0.5                  # a whole wave of negative rows
+    inp["temperature"] = tmp.float()
+    say(f"[parity] temperatures of any sign, {method}")
+    got = run_gpu(w, inp, dtemp=True)
+    h = host_inputs(inp)
+    ref = backward(h["q"], h["k"], h["v"], h["do"], oracle_params(w), h["temp"], h["seg"], h["rb"])
+    check_ml(got["m"], got["l"], ref["m"], ref["l"], "bf16")
+    for n in ("o", "dq", "dk", "dv"):
+        check_tensor(n, got[n], ref[n], "bf16")
+    check_dtemp(got["dtemp"], ref["dtemp"], "bf16")
+
+
 def test_noncausal_window_literal():
     compare_full(W(causal=False, window_len=37, L=260, dtype="f32"))
 
