@@ -40,6 +40,9 @@
 #ifndef ATTN_DQ_BN
 #define ATTN_DQ_BN 32
 #endif
+#ifndef ATTN_PRIO
+#define ATTN_PRIO 1
+#endif
 
 namespace attn {
 
@@ -47,6 +50,21 @@ constexpr int BN16 = ATTN_FWD_BN;   // keys per tile (forward)
 constexpr int BNQ16 = ATTN_DQ_BN;   // keys per tile (dQ: Q and dO fragments stay in registers)
 constexpr int BQ16 = ATTN_DKV_BQ;   // queries per tile (dK/dV)
 constexpr float RESCALE_TAU = 8.f;
+
+// Wave priority around a burst of MFMAs: with two waves per SIMD, the one
+// entering its matrix phase is issued first, so that its MFMAs run while the
+// other wave does vector work.
+__device__ __forceinline__ void mfma_phase(bool begin) {
+  if (ATTN_PRIO) {
+    __builtin_amdgcn_sched_barrier(0);
+    if (begin) {
+      __builtin_amdgcn_s_setprio(1);
+    } else {
+      __builtin_amdgcn_s_setprio(0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
 
 // Segment-skip table: for the workgroup's own rows [r0, r1), flag the tiles of
 // [t_lo, t_hi) (size bt over the other side) that hold an id inside the
@@ -303,6 +321,7 @@ __global__ __launch_bounds__(NTHREADS, ATTN_FWD_WAVES_PER_SIMD) void fwd_bf16_ke
     bf16x8 fk[2][NKB];
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) fk[0][kb] = KT::row_frag(Kt, kb, 0, lane);
+    mfma_phase(true);
 #pragma unroll
     for (int t = 0; t < NT16; ++t) {
       const int cur = t & 1;
@@ -320,6 +339,7 @@ __global__ __launch_bounds__(NTHREADS, ATTN_FWD_WAVES_PER_SIMD) void fwd_bf16_ke
       for (int i = t * NDMA / NT16; i < (t + 1) * NDMA / NT16; ++i) issue_one(jl, st ^ 1, i);
       __builtin_amdgcn_sched_barrier(0);
     }
+    mfma_phase(false);
     load_seg(jl);
     // the tile class is the same on every lane; readfirstlane lets the compiler
     // branch on it instead of running every variant under an exec mask
@@ -341,6 +361,7 @@ __global__ __launch_bounds__(NTHREADS, ATTN_FWD_WAVES_PER_SIMD) void fwd_bf16_ke
     } else {
       fwd_exp<false>(sacc, base, rc, l_run);
     }
+    mfma_phase(true);
 #pragma unroll
     for (int t = 0; t < BN / 16; ++t) {
       // With PRECISE, P enters as hi + lo bf16 parts so that O (and the delta
@@ -358,6 +379,7 @@ __global__ __launch_bounds__(NTHREADS, ATTN_FWD_WAVES_PER_SIMD) void fwd_bf16_ke
         if (PRECISE) oacc[db] = Elem<bf16>::mfma(va, plo, oacc[db]);
       }
     }
+    mfma_phase(false);
     if (jn >= 0) store_seg(st ^ 1);
     wait_vmcnt<0>();
     __syncthreads();
@@ -399,6 +421,7 @@ __device__ __forceinline__ void dq_elementwise(f32x16 (&s)[NKB], const f32x16 (&
                                                const RowC& rc, float dlt, const QMask& qm, int k0,
                                                int hh, const int* sseg, int seg_q, float& tacc) {
   using CapF = Cap<CAP, false>;
+  const float nrd = -rc.R * dlt;
 #pragma unroll
   for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
@@ -412,9 +435,13 @@ __device__ __forceinline__ void dq_elementwise(f32x16 (&s)[NKB], const f32x16 (&
         if (SEG) vis = vis && sseg[koff] == seg_q;
         p = vis ? p : 0.f;
       }
-      const float dsp = p * (dp[kb][r] - dlt);
-      if (DT) tacc = __builtin_fmaf(dsp, __builtin_fmaf(fx, a.kmul, a.kadd), tacc);
-      s[kb][r] = dsp * (rc.R * CapF::g(aux, a));
+      if (DT) {
+        const float dsp = p * (dp[kb][r] - dlt);
+        tacc = __builtin_fmaf(dsp, __builtin_fmaf(fx, a.kmul, a.kadd), tacc);
+      }
+      // R (dP - delta) as one fma against the row constant -R delta (the same
+      // expression with and without DT, so dQ does not depend on it)
+      s[kb][r] = (p * __builtin_fmaf(dp[kb][r], rc.R, nrd)) * CapF::g(aux, a);
     }
   }
 }
@@ -535,6 +562,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void dq_bf16_kernel(KArgs a) {
       fk[0][kb] = KT::row_frag(Kt, kb, 0, lane);
       fv[0][kb] = KT::row_frag(Vt, kb, 0, lane);
     }
+    mfma_phase(true);
 #pragma unroll
     for (int t = 0; t < NT16; ++t) {
       const int cur = t & 1;
@@ -557,6 +585,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void dq_bf16_kernel(KArgs a) {
       for (int i = t * NDMA / NT16; i < (t + 1) * NDMA / NT16; ++i) issue_one(jl, st ^ 1, i);
       __builtin_amdgcn_sched_barrier(0);
     }
+    mfma_phase(false);
     load_seg(jl);
     // the tile class is the same on every lane; readfirstlane lets the compiler
     // branch on it instead of running every variant under an exec mask
@@ -568,6 +597,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void dq_bf16_kernel(KArgs a) {
     } else {
       dq_elementwise<true, true, CAP, DT>(sacc, pacc, a, rc, dlt, qm, k0, hh, sSeg[st], seg_q, tacc);
     }
+    mfma_phase(true);
 #pragma unroll
     for (int t = 0; t < BN / 16; ++t) {
       bf16x8 hi, lo;
@@ -583,6 +613,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void dq_bf16_kernel(KArgs a) {
         if (PRECISE) dqacc[db] = Elem<bf16>::mfma(ka, lo, dqacc[db]);
       }
     }
+    mfma_phase(false);
     if (jn >= 0) store_seg(st ^ 1);
     wait_vmcnt<0>();
     __syncthreads();
@@ -614,7 +645,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void dq_bf16_kernel(KArgs a) {
 // ---------------------------------------------------------------------------
 template <bool MASKED, bool SEG, int CAP, int NQB>
 __device__ __forceinline__ void dkv_elementwise(f32x16 (&s)[NQB], f32x16 (&dp)[NQB], const KArgs& a,
-                                                const float* cKf, const float* cC2, const float* cDl,
+                                                const float* cKf, const float* cC2, const float* cNrd,
                                                 const float* cR, const KMask& km, int q0, int hh,
                                                 const int* sseg, int seg_k) {
   using CapF = Cap<CAP, false>;
@@ -623,7 +654,7 @@ __device__ __forceinline__ void dkv_elementwise(f32x16 (&s)[NQB], f32x16 (&dp)[N
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int qoff = qb * 32 + prow(r, hh);
-      const float Kf = cKf[qoff], C2 = cC2[qoff], dl = cDl[qoff], R = cR[qoff];
+      const float Kf = cKf[qoff], C2 = cC2[qoff], nrd = cNrd[qoff], R = cR[qoff];
       float aux;
       float p = fast_exp2(__builtin_fmaf(CapF::f(s[qb][r], a, aux), Kf, C2));
       if (MASKED) {
@@ -631,7 +662,8 @@ __device__ __forceinline__ void dkv_elementwise(f32x16 (&s)[NQB], f32x16 (&dp)[N
         if (SEG) vis = vis && sseg[qoff] == seg_k;
         p = vis ? p : 0.f;
       }
-      dp[qb][r] = (p * (dp[qb][r] - dl)) * (R * CapF::g(aux, a));
+      // R (dP - delta) as one fma against the query constant -R delta
+      dp[qb][r] = (p * __builtin_fmaf(dp[qb][r], R, nrd)) * CapF::g(aux, a);
       s[qb][r] = p;
     }
   }
@@ -647,7 +679,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void dkv_bf16_kernel(KArgs a) {
   __shared__ __attribute__((aligned(1024))) char sO[2][QT::BYTES];   // dO tile
   __shared__ __attribute__((aligned(16))) float sKf[2][BQ];
   __shared__ __attribute__((aligned(16))) float sC2[2][BQ];
-  __shared__ __attribute__((aligned(16))) float sDl[2][BQ];
+  __shared__ __attribute__((aligned(16))) float sNrd[2][BQ];   // -R delta
   __shared__ __attribute__((aligned(16))) float sR[2][BQ];
   __shared__ int sSeg[2][BQ];
   __shared__ unsigned char sFlag[MAX_TILES];
@@ -751,7 +783,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void dkv_bf16_kernel(KArgs a) {
       const RowC rc = row_consts(a, pT, lse2);
       sKf[stg][cq] = rc.Kf;
       sC2[stg][cq] = rc.C2;
-      sDl[stg][cq] = dlt;
+      sNrd[stg][cq] = -rc.R * dlt;
       sR[stg][cq] = rc.R;
       sSeg[stg][cq] = pSeg;
     }
@@ -812,13 +844,13 @@ __global__ __launch_bounds__(NTHREADS, 1) void dkv_bf16_kernel(KArgs a) {
     auto elementwise = [&](f32x16 (&sa)[1], f32x16 (&pa)[1], int qb) {
       const int o = 32 * qb;
       if (tcls == TILE_FULL) {
-        dkv_elementwise<false, false, CAP>(sa, pa, a, sKf[stg] + o, sC2[stg] + o, sDl[stg] + o,
+        dkv_elementwise<false, false, CAP>(sa, pa, a, sKf[stg] + o, sC2[stg] + o, sNrd[stg] + o,
                                            sR[stg] + o, km, q0 + o, hh, nullptr, 0);
       } else if (!seg_any) {
-        dkv_elementwise<true, false, CAP>(sa, pa, a, sKf[stg] + o, sC2[stg] + o, sDl[stg] + o,
+        dkv_elementwise<true, false, CAP>(sa, pa, a, sKf[stg] + o, sC2[stg] + o, sNrd[stg] + o,
                                           sR[stg] + o, km, q0 + o, hh, nullptr, 0);
       } else {
-        dkv_elementwise<true, true, CAP>(sa, pa, a, sKf[stg] + o, sC2[stg] + o, sDl[stg] + o,
+        dkv_elementwise<true, true, CAP>(sa, pa, a, sKf[stg] + o, sC2[stg] + o, sNrd[stg] + o,
                                          sR[stg] + o, km, q0 + o, hh, sSeg[stg] + o, seg_k);
       }
     };
