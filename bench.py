@@ -34,10 +34,10 @@ HBM_GBPS = 8000.0
 KERNEL_SOURCES = ["attn_bf16.hip", "attn_bf16.h", "attn_device.h", "attn_tiles.h",
                   "attn_internal.h", "attn_bwd_common.h", "attn_preprocess.hip"]
 MEASURED_TRAFFIC = {
-    ("01faa5206e1b1b9c", 5, 0): {"attn_fwd": (384741 * 2.0 + 133120) * 1024,
+    ("da85d392f35aca8c", 5, 0): {"attn_fwd": (230915 * 2.0 + 133159) * 1024,
                                  "attn_bwd_preprocess": (98333 * 2.0 + 4097) * 1024,
-                                 "attn_bwd_dq": (445414 * 2.0 + 131072) * 1024,
-                                 "attn_bwd_dkv": (361397 * 2.0 + 262144) * 1024},
+                                 "attn_bwd_dq": (282835 * 2.0 + 131072) * 1024,
+                                 "attn_bwd_dkv": (361398 * 2.0 + 262144) * 1024},
 }
 
 
