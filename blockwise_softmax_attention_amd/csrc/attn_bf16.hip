@@ -14,6 +14,8 @@
 //   * the forward rescales its accumulator only when a row maximum grows by
 //     more than 2^8 (the exact m is tracked separately), so most tiles skip
 //     the rescale.
+#include <type_traits>
+
 #include "attn_bf16.h"
 #include "attn_bwd_common.h"
 
@@ -304,8 +306,10 @@ __global__ __launch_bounds__(NTHREADS, ATTN_FWD_WAVES_PER_SIMD) void fwd_bf16_ke
   }
   wait_vmcnt<0>();
   __syncthreads();
-  int st = 0;
-  while (j >= 0) {
+  // the loop body once per LDS stage, so that every fragment address is a
+  // per-lane register plus an immediate offset
+  auto step = [&](auto STC) {
+    constexpr int st = decltype(STC)::value;
     const int jn = next_needed(j + 1);
     // tile loaded during this step: the next one, or (without one) the
     // current tile again into the idle stage, which keeps the body branch-free
@@ -383,8 +387,11 @@ __global__ __launch_bounds__(NTHREADS, ATTN_FWD_WAVES_PER_SIMD) void fwd_bf16_ke
     if (jn >= 0) store_seg(st ^ 1);
     wait_vmcnt<0>();
     __syncthreads();
-    st ^= 1;
     j = jn;
+  };
+  while (j >= 0) {
+    step(std::integral_constant<int, 0>{});
+    if (j >= 0) step(std::integral_constant<int, 1>{});
   }
 
   const float l_tot = half_sum(l_run);
@@ -542,8 +549,10 @@ __global__ __launch_bounds__(NTHREADS, 2) void dq_bf16_kernel(KArgs a) {
   }
   wait_vmcnt<0>();
   __syncthreads();
-  int st = 0;
-  while (j >= 0) {
+  // the loop body once per LDS stage, so that every fragment address is a
+  // per-lane register plus an immediate offset
+  auto step = [&](auto STC) {
+    constexpr int st = decltype(STC)::value;
     const int jn = next_needed(j + 1);
     // tile loaded during this step: the next one, or (without one) the
     // current tile again into the idle stage, which keeps the body branch-free
@@ -617,8 +626,11 @@ __global__ __launch_bounds__(NTHREADS, 2) void dq_bf16_kernel(KArgs a) {
     if (jn >= 0) store_seg(st ^ 1);
     wait_vmcnt<0>();
     __syncthreads();
-    st ^= 1;
     j = jn;
+  };
+  while (j >= 0) {
+    step(std::integral_constant<int, 0>{});
+    if (j >= 0) step(std::integral_constant<int, 1>{});
   }
 
   if (DT) {
