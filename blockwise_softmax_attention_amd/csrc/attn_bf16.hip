@@ -45,6 +45,9 @@
 #ifndef ATTN_PRIO
 #define ATTN_PRIO 1
 #endif
+#ifndef DKV_PIN
+#define DKV_PIN 1
+#endif
 
 namespace attn {
 
@@ -915,6 +918,12 @@ __global__ __launch_bounds__(NTHREADS, 1) void dkv_bf16_kernel(KArgs a) {
         }
         s0[0] = Elem<bf16>::mfma(fq[cur], kf[t], s0[0]);
         p0[0] = Elem<bf16>::mfma(fo[cur], vf[t], p0[0]);
+#if DKV_PIN
+        if (t == 0 || t == NT16 - 1) {
+#pragma unroll
+          for (int i = 0; i < NDB; ++i) asm volatile("" : "+a"(dkacc[i]), "+a"(dvacc[i]));
+        }
+#endif
         if (t + 1 < NT16) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
         __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
 #pragma unroll
