@@ -71,12 +71,15 @@ __device__ __forceinline__ void mfma_phase(bool begin) {
   }
 }
 
-// Segment-skip table: for the workgroup's own rows [r0, r1), flag the tiles of
+// Segment tables: for the workgroup's own rows [r0, r1), flag the tiles of
 // [t_lo, t_hi) (size bt over the other side) that hold an id inside the
-// workgroup's [min, max] id range.  Sound for any ids.
+// workgroup's [min, max] id range (flags; sound for any ids), and the tiles
+// that hold an id other than that minimum (mixed).  When the workgroup's rows
+// all share one id and a tile is not mixed, every pair of the tile is in one
+// segment and the segment test can be dropped for it.
 __device__ __forceinline__ void segment_flags(const int* segb, int r0, int r1, int t_lo, int t_hi,
                                               int bt, int L, int tid, unsigned char* flags,
-                                              int* range) {
+                                              unsigned char* mixed, int* range) {
   if (tid == 0) {
     range[0] = 0x7fffffff;
     range[1] = (int)0x80000000;
@@ -87,15 +90,24 @@ __device__ __forceinline__ void segment_flags(const int* segb, int r0, int r1, i
     atomicMin(&range[0], s);
     atomicMax(&range[1], s);
   }
-  for (int t = t_lo + tid; t < t_hi; t += NTHREADS) flags[t - t_lo] = 0;
+  for (int t = t_lo + tid; t < t_hi; t += NTHREADS) flags[t - t_lo] = mixed[t - t_lo] = 0;
   __syncthreads();
   const int smin = range[0], smax = range[1];
   const int end = imin(t_hi * bt, L);
   for (int x = t_lo * bt + tid; x < end; x += NTHREADS) {
     const int s = segb[x];
     if (s >= smin && s <= smax) flags[x / bt - t_lo] = 1;
+    if (s != smin) mixed[x / bt - t_lo] = 1;
   }
   __syncthreads();
+}
+
+// Tile class of a block of tile t of a segment table, the segment test
+// dropped where the table shows a single segment (see segment_flags).
+__device__ __forceinline__ int seg_tile_class(int q0, int q1, int k0, int k1, MaskSpec ms, int t,
+                                              int t_lo, const unsigned char* mixed, const int* range) {
+  if (ms.has_seg && range[0] == range[1] && !mixed[t - t_lo]) ms.has_seg = false;
+  return __builtin_amdgcn_readfirstlane(tile_class(q0, q1, k0, k1, ms));
 }
 
 struct RowItem {
@@ -227,6 +239,7 @@ __global__ __launch_bounds__(NTHREADS, ATTN_FWD_WAVES_PER_SIMD) void fwd_bf16_ke
   __shared__ __attribute__((aligned(1024))) char sV[2][KT::BYTES];
   __shared__ int sSeg[2][BN];
   __shared__ unsigned char sFlag[MAX_TILES];
+  __shared__ unsigned char sMixed[MAX_TILES];
   __shared__ int sRange[2];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -264,7 +277,7 @@ __global__ __launch_bounds__(NTHREADS, ATTN_FWD_WAVES_PER_SIMD) void fwd_bf16_ke
 
   int t_lo = 0, t_hi = 0;
   const bool any = key_tile_range(it.q0, it.q1, BN, ms, &t_lo, &t_hi);
-  if (has_seg && any) segment_flags(segb, it.q0, it.q1, t_lo, t_hi, BN, L, tid, sFlag, sRange);
+  if (has_seg && any) segment_flags(segb, it.q0, it.q1, t_lo, t_hi, BN, L, tid, sFlag, sMixed, sRange);
   auto next_needed = [&](int t) -> int {
     for (; t < t_hi; ++t) {
       if (tile_class(it.q0, it.q1, t * BN, t * BN + BN, ms) == TILE_EMPTY) continue;
@@ -350,7 +363,7 @@ __global__ __launch_bounds__(NTHREADS, ATTN_FWD_WAVES_PER_SIMD) void fwd_bf16_ke
     load_seg(jl);
     // the tile class is the same on every lane; readfirstlane lets the compiler
     // branch on it instead of running every variant under an exec mask
-    const int tcls = __builtin_amdgcn_readfirstlane(tile_class(it.qw0, it.qw0 + 32, k0, k0 + BN, ms));
+    const int tcls = seg_tile_class(it.qw0, it.qw0 + 32, k0, k0 + BN, ms, j, t_lo, sMixed, sRange);
     float mx;
     const bool fdom = tcls == TILE_FULL && mono;
     if (fdom) {
@@ -466,6 +479,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void dq_bf16_kernel(KArgs a) {
   __shared__ __attribute__((aligned(1024))) char sV[2][KT::BYTES];
   __shared__ int sSeg[2][BN];
   __shared__ unsigned char sFlag[MAX_TILES];
+  __shared__ unsigned char sMixed[MAX_TILES];
   __shared__ int sRange[2];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -507,7 +521,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void dq_bf16_kernel(KArgs a) {
 
   int t_lo = 0, t_hi = 0;
   const bool any = key_tile_range(it.q0, it.q1, BN, ms, &t_lo, &t_hi);
-  if (has_seg && any) segment_flags(segb, it.q0, it.q1, t_lo, t_hi, BN, L, tid, sFlag, sRange);
+  if (has_seg && any) segment_flags(segb, it.q0, it.q1, t_lo, t_hi, BN, L, tid, sFlag, sMixed, sRange);
   auto next_needed = [&](int t) -> int {
     for (; t < t_hi; ++t) {
       if (tile_class(it.q0, it.q1, t * BN, t * BN + BN, ms) == TILE_EMPTY) continue;
@@ -601,7 +615,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void dq_bf16_kernel(KArgs a) {
     load_seg(jl);
     // the tile class is the same on every lane; readfirstlane lets the compiler
     // branch on it instead of running every variant under an exec mask
-    const int tcls = __builtin_amdgcn_readfirstlane(tile_class(it.qw0, it.qw0 + 32, k0, k0 + BN, ms));
+    const int tcls = seg_tile_class(it.qw0, it.qw0 + 32, k0, k0 + BN, ms, j, t_lo, sMixed, sRange);
     if (tcls == TILE_FULL) {
       dq_elementwise<false, false, CAP, DT>(sacc, pacc, a, rc, dlt, qm, k0, hh, nullptr, 0, tacc);
     } else if (!seg_any) {
@@ -698,6 +712,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void dkv_bf16_kernel(KArgs a) {
   __shared__ __attribute__((aligned(16))) float sR[2][BQ];
   __shared__ int sSeg[2][BQ];
   __shared__ unsigned char sFlag[MAX_TILES];
+  __shared__ unsigned char sMixed[MAX_TILES];
   __shared__ int sRange[2];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -738,7 +753,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void dkv_bf16_kernel(KArgs a) {
 
   int t_lo = 0, t_hi = 0;
   const bool any = query_tile_range(k0, k1, BQ, ms, &t_lo, &t_hi);
-  if (has_seg && any) segment_flags(segb, k0, k1, t_lo, t_hi, BQ, L, tid, sFlag, sRange);
+  if (has_seg && any) segment_flags(segb, k0, k1, t_lo, t_hi, BQ, L, tid, sFlag, sMixed, sRange);
   auto next_needed = [&](int t) -> int {
     for (; t < t_hi; ++t) {
       if (tile_class(t * BQ, t * BQ + BQ, k0, k1, ms) == TILE_EMPTY) continue;
@@ -855,7 +870,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void dkv_bf16_kernel(KArgs a) {
     static_assert(NQB == 2, "the dK/dV step schedules two 32-query blocks");
     // the tile class is the same on every lane; readfirstlane lets the compiler
     // branch on it instead of running every variant under an exec mask
-    const int tcls = __builtin_amdgcn_readfirstlane(tile_class(q0, q0 + BQ, kw0, kw0 + 32, ms));
+    const int tcls = seg_tile_class(q0, q0 + BQ, kw0, kw0 + 32, ms, tc, t_lo, sMixed, sRange);
     auto elementwise = [&](f32x16 (&sa)[1], f32x16 (&pa)[1], int qb) {
       const int o = 32 * qb;
       if (tcls == TILE_FULL) {

@@ -339,6 +339,26 @@ def test_arbitrary_segment_ids(dtype):
         check_tensor(n, got[n], ref[n], dtype)
 
 
+@pytest.mark.parametrize("D,causal", [(128, True), (64, False)])
+def test_single_segment_tiles(D, causal):
+    """Long runs of one id (tiles inside one segment drop the segment test) next
+    to an id used again further on, ragged boundaries and a mixed tail."""
+    L = 1000
+    w = W(dtype="bf16", D=D, L=L, Hq=4, Hkv=2, causal=causal, temperature=(0.5, 1.5),
+          sm_scale=1 / math.sqrt(D), cap_method="alsc", cap=20.0, alpha=3.0, beta=0.25)
+    inp = make_inputs(w)
+    seg = np.concatenate([np.zeros(300), np.ones(261), np.zeros(199), np.full(180, 2),
+                          np.random.default_rng(5).integers(0, 3, size=L - 940)]).astype(np.int32)
+    inp["segment_ids"] = torch.from_numpy(seg[None, :])
+    say(f"[parity] single-segment tiles D{D} causal={causal}")
+    got = run_gpu(w, inp)
+    h = host_inputs(inp)
+    ref = backward(h["q"], h["k"], h["v"], h["do"], oracle_params(w), h["temp"], h["seg"], h["rb"])
+    check_ml(got["m"], got["l"], ref["m"], ref["l"], "bf16")
+    for n in ("o", "dq", "dk", "dv"):
+        check_tensor(n, got[n], ref[n], "bf16")
+
+
 CAPS = [("none", 0.0, 0.0, 0.0), ("tanh", 5.0, 0.0, 0.0), ("soft_sign", 4.0, 0.0, 0.0),
         ("alsc", 30.0, 4.0, 0.5), ("alsc", 50.0, 2.0, 0.0)]
 
