@@ -34,10 +34,10 @@ HBM_GBPS = 8000.0
 KERNEL_SOURCES = ["attn_bf16.hip", "attn_bf16.h", "attn_device.h", "attn_tiles.h",
                   "attn_internal.h", "attn_bwd_common.h", "attn_preprocess.hip"]
 MEASURED_TRAFFIC = {
-    ("da85d392f35aca8c", 5, 0): {"attn_fwd": (230915 * 2.0 + 133159) * 1024,
+    ("5c5cd5bb99faef25", 5, 0): {"attn_fwd": (234737 * 2.0 + 133823) * 1024,
                                  "attn_bwd_preprocess": (98333 * 2.0 + 4097) * 1024,
-                                 "attn_bwd_dq": (282835 * 2.0 + 131072) * 1024,
-                                 "attn_bwd_dkv": (361398 * 2.0 + 262144) * 1024},
+                                 "attn_bwd_dq": (268297 * 2.0 + 131073) * 1024,
+                                 "attn_bwd_dkv": (361814 * 2.0 + 262144) * 1024},
 }
 
 
