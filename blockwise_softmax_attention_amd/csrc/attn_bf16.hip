@@ -114,14 +114,18 @@ struct RowItem {
   int b, hkv, hq, q0, q1, qw0, qrow;
 };
 
+// Work item -> (batch row, head, query tile).  The batch row varies fastest, so
+// the contiguous run of items each XCD receives (xcd_remap) mixes all batch
+// rows: rows whose masks leave them different amounts of work (ranker bounds,
+// segment lengths) are spread over the XCDs instead of loading some of them.
 __device__ __forceinline__ RowItem decode_row_item(const KArgs& a, int item, int wave, int l32) {
   RowItem it;
-  const int g = item % a.G;
-  int rest = item / a.G;
+  it.b = item % a.B;
+  int rest = item / a.B;
+  const int g = rest % a.G;
+  rest /= a.G;
   const int qt_rev = rest % a.n_q_tiles;
-  rest /= a.n_q_tiles;
-  it.hkv = rest % a.Hkv;
-  it.b = rest / a.Hkv;
+  it.hkv = rest / a.n_q_tiles;
   const int qt = a.causal ? (a.n_q_tiles - 1 - qt_rev) : qt_rev;
   it.hq = it.hkv * a.G + g;
   it.q0 = qt * BM;
@@ -722,10 +726,11 @@ __global__ __launch_bounds__(NTHREADS, 1) void dkv_bf16_kernel(KArgs a) {
   if (item >= a.n_items) return;
 
   const int L = a.L, G = a.G;
-  const int kt = item % a.n_kv_tiles;
-  const int rest = item / a.n_kv_tiles;
-  const int hkv = rest % a.Hkv;
-  const int b = rest / a.Hkv;
+  // batch row fastest (see decode_row_item), then key tile, then KV head
+  const int b = item % a.B;
+  const int rest = item / a.B;
+  const int kt = rest % a.n_kv_tiles;
+  const int hkv = rest / a.n_kv_tiles;
   const int k0 = kt * BKV, k1 = imin(k0 + BKV, L);
   const int kw0 = k0 + wave * 32;
   const int krow = kw0 + l32;
