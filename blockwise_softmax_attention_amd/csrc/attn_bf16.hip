@@ -13,14 +13,18 @@
 //     pairs are all visible and a MASKED path for boundary tiles;
 //   * the forward rescales its accumulator only when a row maximum grows by
 //     more than 2^8 (the exact m is tracked separately), so most tiles skip
-//     the rescale.
+//     the rescale;
+//   * the forward and dQ loops are instantiated once per LDS stage (fragment
+//     addresses become a per-lane register plus an immediate) and raise their
+//     wave priority over MFMA bursts (two waves per SIMD).
 #include <type_traits>
 
 #include "attn_bf16.h"
 #include "attn_bwd_common.h"
 
-// Per-kernel build choices (tile size of the dQ kernel; address laundering,
-// see BTile).
+// Per-kernel build choices: tile sizes, occupancy of the forward, address
+// laundering (see BTile), the MFMA-burst priority (mfma_phase) and the AGPR
+// pins of the dK/dV accumulators.
 #ifndef ATTN_LAUNDER_FWD
 #define ATTN_LAUNDER_FWD 0
 #endif
@@ -45,8 +49,8 @@
 #ifndef ATTN_PRIO
 #define ATTN_PRIO 1
 #endif
-#ifndef DKV_PIN
-#define DKV_PIN 1
+#ifndef ATTN_DKV_PIN
+#define ATTN_DKV_PIN 1
 #endif
 
 namespace attn {
@@ -938,7 +942,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void dkv_bf16_kernel(KArgs a) {
         }
         s0[0] = Elem<bf16>::mfma(fq[cur], kf[t], s0[0]);
         p0[0] = Elem<bf16>::mfma(fo[cur], vf[t], p0[0]);
-#if DKV_PIN
+#if ATTN_DKV_PIN
+        // the dK/dV accumulators stay in AGPRs across this chain (left free,
+        // the allocator parks 32 of them in VGPRs and moves them back each step)
         if (t == 0 || t == NT16 - 1) {
 #pragma unroll
           for (int i = 0; i < NDB; ++i) asm volatile("" : "+a"(dkacc[i]), "+a"(dvacc[i]));
