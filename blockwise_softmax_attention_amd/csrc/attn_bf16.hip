@@ -41,7 +41,7 @@
 #define ATTN_FWD_WAVES_PER_SIMD 2
 #endif
 #ifndef ATTN_DKV_BQ
-#define ATTN_DKV_BQ 64
+#define ATTN_DKV_BQ 128
 #endif
 #ifndef ATTN_DQ_BN
 #define ATTN_DQ_BN 32
@@ -876,7 +876,6 @@ __global__ __launch_bounds__(NTHREADS, 1) void dkv_bf16_kernel(KArgs a) {
     const int q0 = tc * BQ;
     const char* Qt = sQ[stg];
     const char* Ot = sO[stg];
-    static_assert(NQB == 2, "the dK/dV step schedules two 32-query blocks");
     // the tile class is the same on every lane; readfirstlane lets the compiler
     // branch on it instead of running every variant under an exec mask
     const int tcls = seg_tile_class(q0, q0 + BQ, kw0, kw0 + 32, ms, tc, t_lo, sMixed, sRange);
@@ -907,11 +906,10 @@ __global__ __launch_bounds__(NTHREADS, 1) void dkv_bf16_kernel(KArgs a) {
         }
       }
     };
-    // dV / dK unit u = (h, db) of block qb: 2 MFMAs (3 with PRECISE)
-    auto dvdk_unit = [&](int qb, int u, const bf16x8 (&pb)[2], const bf16x8 (&hi)[2],
-                         const bf16x8 (&lo)[2], const bf16x8& oa, const bf16x8& qa) {
+    // dV / dK unit u = (h, db) of a block: 2 MFMAs (3 with PRECISE)
+    auto dvdk_unit = [&](int u, const bf16x8 (&pb)[2], const bf16x8 (&hi)[2], const bf16x8 (&lo)[2],
+                         const bf16x8& oa, const bf16x8& qa) {
       const int h = u / NDB, db = u % NDB;
-      (void)qb;
       dvacc[db] = Elem<bf16>::mfma(oa, pb[h], dvacc[db]);
       dkacc[db] = Elem<bf16>::mfma(qa, hi[h], dkacc[db]);
       if (PRECISE) dkacc[db] = Elem<bf16>::mfma(qa, lo[h], dkacc[db]);
@@ -925,9 +923,16 @@ __global__ __launch_bounds__(NTHREADS, 1) void dkv_bf16_kernel(KArgs a) {
     static_assert(NU == NT16 || NU * 2 == NT16, "units per reduction step");
     constexpr int UPT = NU / NT16 > 0 ? NU / NT16 : 1;   // units per S/dP reduction step
     constexpr int TPU = NT16 / NU > 0 ? NT16 / NU : 1;   // reduction steps per unit
+    // this step's tile loads, spread over the reduction steps of all blocks
+    auto dma = [&](int qb, int t) {
+      constexpr int NS = NQB * NT16;
+#pragma unroll
+      for (int i = (qb * NT16 + t) * NDMA / NS; i < (qb * NT16 + t + 1) * NDMA / NS; ++i)
+        issue_one(gn, tn, stg ^ 1, i);
+    };
 
-    // Block 0: S / dP (two MFMA chains, LDS fragments one step ahead, this
-    // step's tile loads spread over the first half), then its element work.
+    // Block 0: S / dP (two MFMA chains, LDS fragments one step ahead), then
+    // its element work.
     f32x16 s0[1] = {f32x16{}}, p0[1] = {f32x16{}};
     {
       bf16x8 fq[2], fo[2];
@@ -952,59 +957,59 @@ __global__ __launch_bounds__(NTHREADS, 1) void dkv_bf16_kernel(KArgs a) {
 #endif
         if (t + 1 < NT16) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
         __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-#pragma unroll
-        for (int i = t * NDMA / (2 * NT16); i < (t + 1) * NDMA / (2 * NT16); ++i)
-          issue_one(gn, tn, stg ^ 1, i);
+        dma(0, t);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
     fetch_consts(gn, tn);
     elementwise(s0, p0, 0);
-    bf16x8 pb0[2], hi0[2], lo0[2];
-    pack(s0[0], p0[0], pb0, hi0, lo0);
-    // Block 1's S / dP with block 0's dV / dK between them: ~10 independent
-    // MFMA chains in flight, and only one block's S / dP accumulators live.
-    f32x16 s1[1] = {f32x16{}}, p1[1] = {f32x16{}};
-    {
-      bf16x8 fq[2], fo[2], ta[2], tb[2];
-      fq[0] = QT::row_frag(Qt, 1, 0, lane);
-      fo[0] = QT::row_frag(Ot, 1, 0, lane);
-      tr_pair(0, 0, ta[0], tb[0]);
+    bf16x8 pbp[2], hip[2], lop[2];   // P and dS of the previous block
+    pack(s0[0], p0[0], pbp, hip, lop);
+    // Blocks 1 ..: each block's S / dP with the previous block's dV / dK
+    // between them (~10 independent MFMA chains in flight; only one block's
+    // S / dP accumulators live), then its element work.
 #pragma unroll
-      for (int t = 0; t < NT16; ++t) {
-        const int cur = t & 1;
-        if (t + 1 < NT16) {
-          fq[cur ^ 1] = QT::row_frag(Qt, 1, t + 1, lane);
-          fo[cur ^ 1] = QT::row_frag(Ot, 1, t + 1, lane);
-        }
-        s1[0] = Elem<bf16>::mfma(fq[cur], kf[t], s1[0]);
-        p1[0] = Elem<bf16>::mfma(fo[cur], vf[t], p1[0]);
-        if (t % TPU == 0) {
+    for (int qb = 1; qb < NQB; ++qb) {
+      f32x16 s1[1] = {f32x16{}}, p1[1] = {f32x16{}};
+      {
+        bf16x8 fq[2], fo[2], ta[2], tb[2];
+        fq[0] = QT::row_frag(Qt, qb, 0, lane);
+        fo[0] = QT::row_frag(Ot, qb, 0, lane);
+        tr_pair(qb - 1, 0, ta[0], tb[0]);
 #pragma unroll
-          for (int k = 0; k < UPT; ++k) {
-            const int u = (t / TPU) * UPT + k;
-            const int c = u & 1;
-            if (u + 1 < NU) tr_pair(0, u + 1, ta[c ^ 1], tb[c ^ 1]);
-            dvdk_unit(0, u, pb0, hi0, lo0, ta[c], tb[c]);
+        for (int t = 0; t < NT16; ++t) {
+          const int cur = t & 1;
+          if (t + 1 < NT16) {
+            fq[cur ^ 1] = QT::row_frag(Qt, qb, t + 1, lane);
+            fo[cur ^ 1] = QT::row_frag(Ot, qb, t + 1, lane);
           }
-        }
+          s1[0] = Elem<bf16>::mfma(fq[cur], kf[t], s1[0]);
+          p1[0] = Elem<bf16>::mfma(fo[cur], vf[t], p1[0]);
+          if (t % TPU == 0) {
 #pragma unroll
-        for (int i = NDMA / 2 + t * NDMA / (2 * NT16); i < NDMA / 2 + (t + 1) * NDMA / (2 * NT16); ++i)
-          issue_one(gn, tn, stg ^ 1, i);
-        __builtin_amdgcn_sched_barrier(0);
+            for (int k = 0; k < UPT; ++k) {
+              const int u = (t / TPU) * UPT + k;
+              const int c = u & 1;
+              if (u + 1 < NU) tr_pair(qb - 1, u + 1, ta[c ^ 1], tb[c ^ 1]);
+              dvdk_unit(u, pbp, hip, lop, ta[c], tb[c]);
+            }
+          }
+          dma(qb, t);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
+      elementwise(s1, p1, qb);
+      pack(s1[0], p1[0], pbp, hip, lop);
     }
-    elementwise(s1, p1, 1);
+    // the last block's dV / dK
     {
-      bf16x8 pb1[2], hi1[2], lo1[2];
-      pack(s1[0], p1[0], pb1, hi1, lo1);
       bf16x8 ta[2], tb[2];
-      tr_pair(1, 0, ta[0], tb[0]);
+      tr_pair(NQB - 1, 0, ta[0], tb[0]);
 #pragma unroll
       for (int u = 0; u < NU; ++u) {
         const int c = u & 1;
-        if (u + 1 < NU) tr_pair(1, u + 1, ta[c ^ 1], tb[c ^ 1]);
-        dvdk_unit(1, u, pb1, hi1, lo1, ta[c], tb[c]);
+        if (u + 1 < NU) tr_pair(NQB - 1, u + 1, ta[c ^ 1], tb[c ^ 1]);
+        dvdk_unit(u, pbp, hip, lop, ta[c], tb[c]);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
