@@ -59,6 +59,9 @@ def parse():
     ap.add_argument("--precise-ds", type=int, default=-1,
                     help="1: hi+lo bf16 P and dS; 0: single bf16; -1 (default): 0 for the "
                          "workloads whose full-size parity tests run in that mode (4, 5), else 1")
+    ap.add_argument("--stored-ds", type=int, default=-1,
+                    help="1: stored-dS backward (dK/dV stores dS, dQ = dS K); 0: recomputing dQ; "
+                         "-1 (default): 1 wherever it applies (bf16, single-bf16 dS)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-len", type=int, default=16384,
                     help="prefix length of the oracle's bounded sample")
@@ -138,8 +141,11 @@ def main():
     q, k, v, do = dev["q"], dev["k"], dev["v"], dev["do"]
     temp, seg, rb = dev["temperature"], dev["segment_ids"], dev["ranker_bounds"]
     stream = torch.cuda.current_stream()
+    stored = ba.stored_ds_eligible(p) if args.stored_ds < 0 else bool(args.stored_ds)
+    ws = ba.ds_workspace(p, "cuda") if stored else None
 
-    names = ["attn_fwd", "attn_bwd_preprocess", "attn_bwd_dq", "attn_bwd_dkv"]
+    names = (["attn_fwd", "attn_bwd_preprocess", "attn_bwd_dkv_ds", "attn_bwd_dq_ds"] if stored else
+             ["attn_fwd", "attn_bwd_preprocess", "attn_bwd_dq", "attn_bwd_dkv"])
 
     def step(ev=None):
         if ev is not None:
@@ -150,10 +156,16 @@ def main():
         ba.attn_bwd_preprocess(p, o, do, delta, stream=stream)
         if ev is not None:
             ev[2].record(stream)
-        ba.attn_bwd_dq(p, q, k, v, do, m, l, delta, temp, seg, rb, dq, stream=stream)
-        if ev is not None:
-            ev[3].record(stream)
-        ba.attn_bwd_dkv(p, q, k, v, do, m, l, delta, temp, seg, rb, dk, dv, stream=stream)
+        if stored:
+            ba.attn_bwd_dkv_ds(p, q, k, v, do, m, l, delta, ws, temp, seg, rb, dk, dv, stream=stream)
+            if ev is not None:
+                ev[3].record(stream)
+            ba.attn_bwd_dq_ds(p, k, ws, seg, rb, dq, stream=stream)
+        else:
+            ba.attn_bwd_dq(p, q, k, v, do, m, l, delta, temp, seg, rb, dq, stream=stream)
+            if ev is not None:
+                ev[3].record(stream)
+            ba.attn_bwd_dkv(p, q, k, v, do, m, l, delta, temp, seg, rb, dk, dv, stream=stream)
         if ev is not None:
             ev[4].record(stream)
 
@@ -175,7 +187,7 @@ def main():
     avg = {n: sum(x) / len(x) for n, x in per.items()}
     step_ms = wall * 1e3 / args.steps
     fwd_ms = avg["attn_fwd"]
-    bwd_ms = avg["attn_bwd_preprocess"] + avg["attn_bwd_dq"] + avg["attn_bwd_dkv"]
+    bwd_ms = sum(avg[n] for n in names[1:])
     value = (fwd_flop + bwd_flop) / (step_ms * 1e-3) / 1e12
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
 
@@ -184,9 +196,12 @@ def main():
     # Per visible pair and query head: fwd 4 D (QK^T, PV); dq 6 D (QK^T, dO V^T,
     # dS K); dkv 8 D (QK^T, dO V^T, P^T dO, dS^T Q).  Preprocess is HBM-bound:
     # reads O (f32) and dO, writes delta.
+    # With the stored-dS backward the dK/dV kernel does the same MFMA work and
+    # dQ = dS K (2 D per pair) streams the stored dS from HBM.
     alg = {"attn_fwd": 4.0 * D * pairs, "attn_bwd_dq": 6.0 * D * pairs,
-           "attn_bwd_dkv": 8.0 * D * pairs}
-    dom = max(alg, key=lambda n: avg[n])
+           "attn_bwd_dkv": 8.0 * D * pairs, "attn_bwd_dkv_ds": 8.0 * D * pairs,
+           "attn_bwd_dq_ds": 2.0 * D * pairs}
+    dom = max((n for n in names if n in alg), key=lambda n: avg[n])
     achieved = alg[dom] / (avg[dom] * 1e-3) / 1e12
     pre_bytes = B * L * Hq * D * (4 + (2 if w.dtype == "bf16" else 4)) + B * Hq * L * 4
     measured = MEASURED_TRAFFIC.get((kernel_source_hash(), args.workload, precise))
@@ -202,7 +217,7 @@ def main():
         "dtype": w.dtype, "data": "synthetic",
         "config": {"workload": w.name, "batch": B, "seq_len": L, "q_heads": Hq, "kv_heads": Hkv,
                    "head_dim": D, "cap": w.cap_method, "causal": w.causal, "window": w.window_len,
-                   "precise_ds": bool(precise), "visible_pairs": pairs},
+                   "precise_ds": bool(precise), "stored_ds": stored, "visible_pairs": pairs},
         "pct_peak": round(100.0 * value / peak, 2),
         "fwd": {"ms": round(fwd_ms, 4), "tflops": round(fwd_flop / (fwd_ms * 1e-3) / 1e12, 2),
                 "pct_peak": round(100.0 * fwd_flop / (fwd_ms * 1e-3) / 1e12 / peak, 2)},
@@ -210,6 +225,9 @@ def main():
                 "pct_peak": round(100.0 * bwd_flop / (bwd_ms * 1e-3) / 1e12 / peak, 2)},
         "kernels_ms": {n: round(avg[n], 4) for n in names},
         "preprocess_gbps": round(pre_bytes / (avg["attn_bwd_preprocess"] * 1e-3) / 1e9, 1),
+        # stored-dS dQ: workspace bytes (every band tile; tiles skipped by a mask
+        # are not read, so this bounds the dS bytes streamed) per launch time
+        "dq_ds_gbps": (round(ws.numel() / (avg["attn_bwd_dq_ds"] * 1e-3) / 1e9, 1) if stored else None),
         "roofline": roofline,
     }
     if not args.no_cpu_baseline:

@@ -6,7 +6,8 @@ memory and the current HIP stream.  There is no fallback: if the library is
 missing or the tensors are not on the GPU, the calls raise.
 
 Names mirror the C ABI: attn_fwd, attn_bwd_preprocess, attn_bwd_dq,
-attn_bwd_dkv, attn_plan_count, attn_check_params.
+attn_bwd_dkv, attn_bwd_ds_workspace_size, attn_bwd_dkv_ds, attn_bwd_dq_ds,
+attn_reduce_heads, attn_ranker_bounds, attn_plan_count, attn_check_params.
 """
 from __future__ import annotations
 
@@ -81,6 +82,10 @@ _FN_SIGS = {
     "attn_plan_count": [ctypes.POINTER(_CParams), _P, _P, ctypes.POINTER(ctypes.c_int64),
                         ctypes.POINTER(ctypes.c_int64)],
     "attn_check_params": [ctypes.POINTER(_CParams)],
+    "attn_bwd_ds_workspace_size": [ctypes.POINTER(_CParams), ctypes.POINTER(ctypes.c_uint64)],
+    "attn_bwd_dkv_ds": [ctypes.POINTER(_CParams), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                        _P],
+    "attn_bwd_dq_ds": [ctypes.POINTER(_CParams), _P, _P, _P, _P, _P, _P],
 }
 
 
@@ -221,6 +226,55 @@ def attn_bwd_dkv(p: AttnParams, q, k, v, d_o, m, l, delta, temperature=None, seg
     return dk, dv
 
 
+def attn_bwd_ds_workspace_size(p: AttnParams) -> int:
+    """Bytes of the stored-dS workspace (bf16 inputs, precise_ds off)."""
+    n = ctypes.c_uint64(0)
+    cp = p.to_c()
+    _check(load_library().attn_bwd_ds_workspace_size(ctypes.byref(cp), ctypes.byref(n)))
+    return int(n.value)
+
+
+def ds_workspace(p: AttnParams, device) -> torch.Tensor:
+    """A workspace tensor for attn_bwd_dkv_ds / attn_bwd_dq_ds."""
+    return torch.empty(attn_bwd_ds_workspace_size(p), dtype=torch.uint8, device=device)
+
+
+def attn_bwd_dkv_ds(p: AttnParams, q, k, v, d_o, m, l, delta, ds, temperature=None, segment_ids=None,
+                    ranker_bounds=None, dk=None, dv=None, stream=None):
+    """dK, dV as attn_bwd_dkv, and dS stored into the workspace ds."""
+    shape = (p.batch, p.seq_len, p.kv_heads, p.head_dim)
+    dk = torch.empty(shape, dtype=torch.float32, device=q.device) if dk is None else dk
+    dv = torch.empty(shape, dtype=torch.float32, device=q.device) if dv is None else dv
+    dt = _in_dtype(p)
+    cp = p.to_c()
+    _check(load_library().attn_bwd_dkv_ds(
+        ctypes.byref(cp), _ptr(q, "q", dt), _ptr(k, "k", dt), _ptr(v, "v", dt),
+        _ptr(temperature, "temperature", torch.float32), _ptr(segment_ids, "segment_ids", torch.int32),
+        _ptr(ranker_bounds, "ranker_bounds", torch.int32), _ptr(d_o, "d_o", dt),
+        _ptr(m, "m", torch.float32), _ptr(l, "l", torch.float32), _ptr(delta, "delta", torch.float32),
+        _ptr(dk, "dk", torch.float32), _ptr(dv, "dv", torch.float32), _ptr(ds, "ds", torch.uint8),
+        _stream(stream)))
+    return dk, dv
+
+
+def attn_bwd_dq_ds(p: AttnParams, k, ds, segment_ids=None, ranker_bounds=None, dq=None, stream=None):
+    """dQ = dS K from the workspace written by attn_bwd_dkv_ds."""
+    dq = torch.empty((p.batch, p.seq_len, p.q_heads, p.head_dim), dtype=torch.float32,
+                     device=k.device) if dq is None else dq
+    cp = p.to_c()
+    _check(load_library().attn_bwd_dq_ds(
+        ctypes.byref(cp), _ptr(k, "k", _in_dtype(p)), _ptr(segment_ids, "segment_ids", torch.int32),
+        _ptr(ranker_bounds, "ranker_bounds", torch.int32), _ptr(ds, "ds", torch.uint8),
+        _ptr(dq, "dq", torch.float32), _stream(stream)))
+    return dq
+
+
+def stored_ds_eligible(p: AttnParams, dtemp: bool = False) -> bool:
+    """The stored-dS backward applies: bf16 inputs, single-bf16 dS, no
+    temperature gradient (which the recomputing dQ kernel forms)."""
+    return p.dtype == ATTN_BF16 and not p.precise_ds and not dtemp
+
+
 def attn_plan_count(p: AttnParams, segment_ids=None, ranker_bounds=None):
     """(unmasked pairs, visited forward tiles), both summed over batch and heads.
     Host-side; segment_ids / ranker_bounds are CPU int32 tensors or None."""
@@ -243,16 +297,30 @@ def attn_plan_count(p: AttnParams, segment_ids=None, ranker_bounds=None):
 
 
 def attention_forward_backward(p: AttnParams, q, k, v, d_o, temperature=None, segment_ids=None,
-                               ranker_bounds=None, dtemp: bool = False, stream=None):
+                               ranker_bounds=None, dtemp: bool = False, stream=None,
+                               stored_ds: Optional[bool] = None):
     """One pass of the whole path: forward, then preprocess, dQ and dK/dV
-    (and, with dtemp=True, the temperature gradient (B, L))."""
+    (and, with dtemp=True, the temperature gradient (B, L)).  stored_ds: use
+    the stored-dS backward (dK/dV, then dQ from the stored dS); None picks it
+    whenever it applies (stored_ds_eligible)."""
     o, m, l = attn_fwd(p, q, k, v, temperature, segment_ids, ranker_bounds, stream=stream)
     delta = attn_bwd_preprocess(p, o, d_o, stream=stream)
-    res = attn_bwd_dq(p, q, k, v, d_o, m, l, delta, temperature, segment_ids, ranker_bounds,
-                      dtemp_h=True if dtemp else None, stream=stream)
-    dq, dtemp_h = res if dtemp else (res, None)
-    dk, dv = attn_bwd_dkv(p, q, k, v, d_o, m, l, delta, temperature, segment_ids, ranker_bounds,
-                          stream=stream)
+    if stored_ds is None:
+        stored_ds = stored_ds_eligible(p, dtemp)
+    if stored_ds:
+        if dtemp:
+            raise ValueError("the temperature gradient needs the recomputing dQ (stored_ds=False)")
+        ds = ds_workspace(p, q.device)
+        dk, dv = attn_bwd_dkv_ds(p, q, k, v, d_o, m, l, delta, ds, temperature, segment_ids,
+                                 ranker_bounds, stream=stream)
+        dq = attn_bwd_dq_ds(p, k, ds, segment_ids, ranker_bounds, stream=stream)
+        dtemp_h = None
+    else:
+        res = attn_bwd_dq(p, q, k, v, d_o, m, l, delta, temperature, segment_ids, ranker_bounds,
+                          dtemp_h=True if dtemp else None, stream=stream)
+        dq, dtemp_h = res if dtemp else (res, None)
+        dk, dv = attn_bwd_dkv(p, q, k, v, d_o, m, l, delta, temperature, segment_ids, ranker_bounds,
+                              stream=stream)
     out = dict(o=o, m=m, l=l, delta=delta, dq=dq, dk=dk, dv=dv)
     if dtemp:
         out["dtemp_h"] = dtemp_h

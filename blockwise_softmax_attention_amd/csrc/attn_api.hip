@@ -293,6 +293,72 @@ attn_status attn_bwd_dkv(const attn_params* p, const void* q, const void* k, con
                     "attn_bwd_dkv launch");
 }
 
+static attn_status check_ds_params(const attn_params* p) {
+  ATTN_TRY(check_params(p));
+  if (p->dtype != ATTN_BF16)
+    return fail(ATTN_ERR_DTYPE, "the stored-dS backward takes bfloat16 inputs");
+  if (p->precise_ds != 0)
+    return fail(ATTN_ERR_UNSUPPORTED, "the stored-dS backward stores a single bf16 dS: precise_ds must be 0");
+  return ATTN_OK;
+}
+
+static long long ds_slots(const attn_params* p) {
+  return attn::ds_slots_per_head(attn::ds_band(p->seq_len, p->causal != 0, p->window_len));
+}
+
+attn_status attn_bwd_ds_workspace_size(const attn_params* p, uint64_t* bytes) {
+  ATTN_TRY(check_ds_params(p));
+  if (bytes == nullptr) return fail(ATTN_ERR_NULL_PTR, "bytes is NULL");
+  const long long tiles = (long long)p->batch * p->q_heads * ds_slots(p);
+  if (tiles > (1LL << 40)) return fail(ATTN_ERR_SHAPE, "stored-dS workspace too large");
+  *bytes = (uint64_t)tiles * attn::DS_ELEMS * 2;
+  return ATTN_OK;
+}
+
+attn_status attn_bwd_dkv_ds(const attn_params* p, const void* q, const void* k, const void* v,
+                            const float* temperature, const int32_t* segment_ids,
+                            const int32_t* ranker_bounds, const void* d_o, const float* m,
+                            const float* l, const float* delta, float* dk, float* dv, void* ds,
+                            void* stream) {
+  ATTN_TRY(check_ds_params(p));
+  ATTN_TRY(check_bwd_inputs(p, q, k, v, temperature, segment_ids, ranker_bounds, d_o, m, l, delta));
+  ATTN_TRY(check_ptr(dk, "dk", 16));
+  ATTN_TRY(check_ptr(dv, "dv", 16));
+  ATTN_TRY(check_ptr(ds, "ds", 16));
+  attn::KArgs a = make_args(p, temperature, segment_ids, ranker_bounds);
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.dout = d_o;
+  a.m_in = m;
+  a.l_in = l;
+  a.delta_in = delta;
+  a.out0 = dk;
+  a.out1 = dv;
+  a.ds = ds;
+  a.ds_slots = ds_slots(p);
+  a.n_items = a.B * a.Hkv * a.n_kv_tiles;
+  return hip_status(attn::launch_dkv_ds_bf16(a, p->head_dim, effective_cap(p), (hipStream_t)stream),
+                    "attn_bwd_dkv_ds launch");
+}
+
+attn_status attn_bwd_dq_ds(const attn_params* p, const void* k, const int32_t* segment_ids,
+                           const int32_t* ranker_bounds, const void* ds, float* dq, void* stream) {
+  ATTN_TRY(check_ds_params(p));
+  ATTN_TRY(check_common(p, nullptr, segment_ids, ranker_bounds));
+  ATTN_TRY(check_ptr(k, "k", 16));
+  ATTN_TRY(check_ptr(ds, "ds", 16));
+  ATTN_TRY(check_ptr(dq, "dq", 16));
+  attn::KArgs a = make_args(p, nullptr, segment_ids, ranker_bounds);
+  a.k = k;
+  a.ds = const_cast<void*>(ds);
+  a.ds_slots = ds_slots(p);
+  a.out0 = dq;
+  a.n_items = a.B * a.Hq * a.n_q_tiles;
+  return hip_status(attn::launch_dq_ds_bf16(a, p->head_dim, (hipStream_t)stream),
+                    "attn_bwd_dq_ds launch");
+}
+
 attn_status attn_plan_count(const attn_params* p, const int32_t* seg, const int32_t* bounds,
                             int64_t* unmasked_pairs, int64_t* visited_tiles) {
   ATTN_TRY(check_params(p));

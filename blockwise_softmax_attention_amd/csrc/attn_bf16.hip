@@ -19,6 +19,7 @@
 //     wave priority over MFMA bursts (two waves per SIMD).
 #include <type_traits>
 
+#include "attn.h"
 #include "attn_bf16.h"
 #include "attn_bwd_common.h"
 
@@ -76,14 +77,19 @@ __device__ __forceinline__ void mfma_phase(bool begin) {
 }
 
 // Segment tables: for the workgroup's own rows [r0, r1), flag the tiles of
-// [t_lo, t_hi) (size bt over the other side) that hold an id inside the
-// workgroup's [min, max] id range (flags; sound for any ids), and the tiles
-// that hold an id other than that minimum (mixed).  When the workgroup's rows
-// all share one id and a tile is not mixed, every pair of the tile is in one
-// segment and the segment test can be dropped for it.
+// [t_lo, t_hi) (size bt over the other side) that can share a segment with
+// them, and the tiles that hold an id other than the workgroup's minimum
+// (mixed).  When the workgroup's rows all share one id and a tile is not
+// mixed, every pair of the tile is in one segment and the segment test can be
+// dropped for it.  The flag test is either "the tile holds an id inside the
+// workgroup's [min, max]" (flags only) or, with a second table, the symmetric
+// "the tile's [min, max] and the workgroup's overlap" (flags && flags2: some
+// id <= max and some id >= min), which the query-tile and key-tile sides of
+// the stored-dS backward evaluate identically; both are sound for any ids.
 __device__ __forceinline__ void segment_flags(const int* segb, int r0, int r1, int t_lo, int t_hi,
                                               int bt, int L, int tid, unsigned char* flags,
-                                              unsigned char* mixed, int* range) {
+                                              unsigned char* mixed, int* range,
+                                              unsigned char* flags2 = nullptr) {
   if (tid == 0) {
     range[0] = 0x7fffffff;
     range[1] = (int)0x80000000;
@@ -94,13 +100,21 @@ __device__ __forceinline__ void segment_flags(const int* segb, int r0, int r1, i
     atomicMin(&range[0], s);
     atomicMax(&range[1], s);
   }
-  for (int t = t_lo + tid; t < t_hi; t += NTHREADS) flags[t - t_lo] = mixed[t - t_lo] = 0;
+  for (int t = t_lo + tid; t < t_hi; t += NTHREADS) {
+    flags[t - t_lo] = mixed[t - t_lo] = 0;
+    if (flags2 != nullptr) flags2[t - t_lo] = 0;
+  }
   __syncthreads();
   const int smin = range[0], smax = range[1];
   const int end = imin(t_hi * bt, L);
   for (int x = t_lo * bt + tid; x < end; x += NTHREADS) {
     const int s = segb[x];
-    if (s >= smin && s <= smax) flags[x / bt - t_lo] = 1;
+    if (flags2 != nullptr) {
+      if (s <= smax) flags[x / bt - t_lo] = 1;
+      if (s >= smin) flags2[x / bt - t_lo] = 1;
+    } else if (s >= smin && s <= smax) {
+      flags[x / bt - t_lo] = 1;
+    }
     if (s != smin) mixed[x / bt - t_lo] = 1;
   }
   __syncthreads();
@@ -678,6 +692,166 @@ __global__ __launch_bounds__(NTHREADS, 2) void dq_bf16_kernel(KArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// dQ from stored dS
+// ---------------------------------------------------------------------------
+// dQ^T += K^T dS^T over the visited key tiles of the workgroup's query tile,
+// dS taken from the tiles the dK/dV kernel stored (WDS): no recomputation of
+// S, P or dP and no element work, so the kernel streams the stored tiles from
+// HBM.  Both operands reduce over keys and are read transposed from LDS
+// (ds_read_b64_tr_b16): the K tile (columns = d) and the key-major dS tile
+// (columns = queries; wave w takes its 32).  NST LDS stages, NST - 1 steps of
+// loads in flight; every step issues the same number of loads (without a
+// further step it refetches its own tiles into the idle stage), so one
+// vmcnt wait finds exactly the loads of the step about to run.
+constexpr int DQS_BN = 64;    // keys per step: half a stored tile
+constexpr int DQS_NST = 4;    // LDS stages
+constexpr int DQS_FLAGS = ATTN_MAX_SEQ_LEN_SEGMENTS / DS_T;
+
+template <int D>
+__global__ __launch_bounds__(NTHREADS, 1) void dq_ds_bf16_kernel(KArgs a) {
+  constexpr int BN = DQS_BN, NST = DQS_NST, HALVES = DS_T / BN;
+  using KT = BTile<BN, D, NWAVES>;
+  using ST = BTile<BN, DS_T, NWAVES>;
+  constexpr int NDB = D / 32, NDMA = KT::PER_WAVE + ST::PER_WAVE;
+  static_assert(BM == DS_T, "a workgroup's query tile is one stored query tile");
+
+  __shared__ __attribute__((aligned(1024))) char sK[NST][KT::BYTES];
+  __shared__ __attribute__((aligned(1024))) char sS[NST][ST::BYTES];
+  __shared__ unsigned char sFlag[DQS_FLAGS];
+  __shared__ unsigned char sFlag2[DQS_FLAGS];
+  __shared__ unsigned char sMixed[DQS_FLAGS];
+  __shared__ int sRange[2];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, hh = lane >> 5;
+  const int item = xcd_remap(blockIdx.x, gridDim.x);
+  if (item >= a.n_items) return;
+  const RowItem it = decode_row_item(a, item, wave, l32);
+  const int L = a.L, b = it.b, qrow = it.qrow;
+  const int qt = it.q0 / DS_T;
+
+  const long kv_rs = (long)a.Hkv * D;
+  const uint32_t kv_rsb = (uint32_t)(kv_rs * sizeof(bf16));
+  constexpr uint32_t S_RSB = DS_T * sizeof(bf16);
+  const typename KT::Lane kln = KT::lane_of(kv_rsb, lane, wave);
+  const typename ST::Lane sln = ST::lane_of(S_RSB, lane, wave);
+  const bf16* Kb = (const bf16*)a.k + ((long)b * L * a.Hkv + it.hkv) * D;
+  const DsBand band = ds_band(L, a.causal, a.window);
+  const int t_lo = ds_lo(qt, band), t_hi = ds_hi(qt, band);
+  const bf16* Sb = (const bf16*)a.ds +
+                   (((long long)b * a.Hq + it.hq) * a.ds_slots + ds_offset(qt, band)) * DS_ELEMS;
+
+  const MaskSpec ms = load_mask_spec(a, b);
+  const bool has_seg = ms.has_seg;
+  const int* segb = has_seg ? a.seg + (long)b * L : nullptr;
+  if (has_seg)
+    segment_flags(segb, it.q0, it.q1, t_lo, t_hi, DS_T, L, tid, sFlag, sMixed, sRange, sFlag2);
+  // the blocks the dK/dV kernel visited (and stored): the same tile class and
+  // symmetric segment test, evaluated from the query side
+  auto next_tile = [&](int t) -> int {
+    for (; t < t_hi; ++t) {
+      if (tile_class(it.q0, it.q1, t * DS_T, t * DS_T + DS_T, ms) == TILE_EMPTY) continue;
+      if (has_seg && !(sFlag[t - t_lo] && sFlag2[t - t_lo])) continue;
+      return t;
+    }
+    return -1;
+  };
+  // steps: (key tile, half) with the half's first key inside the sequence;
+  // kt >= 0 on entry, -1 on return after the last step
+  auto next_step = [&](int& kt, int& hf) {
+    if (hf + 1 < HALVES && kt * DS_T + (hf + 1) * BN < L) {
+      ++hf;
+      return;
+    }
+    kt = next_tile(kt + 1);
+    hf = 0;
+  };
+  auto issue_one = [&](int kt, int hf, int stg, int i) {
+    const int kr0 = kt * DS_T + hf * BN;
+    if (i < KT::PER_WAVE) {
+      KT::issue_one(lds_offset(sK[stg]), Kb + (long)kr0 * kv_rs, kv_rsb, L - kr0, kln, wave, i);
+    } else {
+      ST::issue_one(lds_offset(sS[stg]), Sb + ((long)(kt - t_lo) * DS_ELEMS + (long)hf * BN * DS_T),
+                    S_RSB, BN, sln, wave, i - KT::PER_WAVE);
+    }
+  };
+  auto issue = [&](int kt, int hf, int stg) {
+#pragma unroll
+    for (int i = 0; i < NDMA; ++i) issue_one(kt, hf, stg, i);
+  };
+
+  f32x16 dqacc[NDB];
+#pragma unroll
+  for (int i = 0; i < NDB; ++i) dqacc[i] = f32x16{};
+
+  // prologue: steps 0 .. NST-2 into stages 0 .. NST-2 (the last real step
+  // repeated where there are fewer)
+  int ck = next_tile(t_lo), ch = 0;
+  int lk = ck, lh = ch;   // last step issued
+  if (ck >= 0) {
+    issue(ck, ch, 0);
+#pragma unroll
+    for (int s = 1; s < NST - 1; ++s) {
+      int nk = lk, nh = lh;
+      next_step(nk, nh);
+      if (nk >= 0) {
+        lk = nk;
+        lh = nh;
+      }
+      issue(lk, lh, s);
+    }
+  }
+  int fk = lk, fh = lh;   // frontier: the next step to issue follows it
+  bool fdone = false;
+  int stg = 0;
+  while (ck >= 0) {
+    wait_vmcnt<NDMA * (NST - 2)>();
+    __syncthreads();
+    // loads of step + NST - 1 into the stage freed by the previous step
+    {
+      int nk = fk, nh = fh;
+      if (!fdone) next_step(nk, nh);
+      if (nk >= 0 && !fdone) {
+        fk = nk;
+        fh = nh;
+      } else {
+        fdone = true;
+      }
+      issue(fk, fh, (stg + NST - 1) % NST);
+    }
+    const char* Kt = sK[stg];
+    const char* St = sS[stg];
+#pragma unroll
+    for (int t = 0; t < BN / 16; ++t) {
+      const bf16x8 sf = ST::tr_frag(St, wave, t, lane);
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const bf16x8 ka = KT::tr_frag(Kt, db, t, lane);
+        dqacc[db] = Elem<bf16>::mfma(ka, sf, dqacc[db]);
+      }
+    }
+    next_step(ck, ch);
+    stg = (stg + 1) % NST;
+  }
+  wait_vmcnt<0>();
+
+  if (qrow < L) {
+    float* drow = a.out0 + ((long)(b * L + qrow) * a.Hq + it.hq) * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        f32x4 v;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) v[c] = dqacc[db][4 * r4 + c];
+        *(f32x4*)(drow + 32 * db + 8 * r4 + 4 * hh) = v;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // dK / dV
 // ---------------------------------------------------------------------------
 template <bool MASKED, bool SEG, int CAP, int NQB>
@@ -706,8 +880,14 @@ __device__ __forceinline__ void dkv_elementwise(f32x16 (&s)[NQB], f32x16 (&dp)[N
   }
 }
 
-template <int D, int CAP, bool PRECISE>
+// WDS: also store this step's bf16 dS, key-major, into the stored-dS
+// workspace (slot of block (query tile, key tile), see ds_slot), for the dQ
+// kernel of the stored-dS backward; the segment skip then takes the symmetric
+// test of segment_flags, which that kernel evaluates the same way.
+template <int D, int CAP, bool PRECISE, bool WDS>
 __global__ __launch_bounds__(NTHREADS, 1) void dkv_bf16_kernel(KArgs a) {
+  static_assert(!(WDS && PRECISE), "the stored dS is a single bf16");
+  static_assert(!WDS || (BQ16 == DS_T && BKV == DS_T), "stored tiles are the dK/dV query and key tiles");
   constexpr int BQ = BQ16;
   using QT = BTile<BQ, D, NWAVES, ATTN_LAUNDER_DKV>;
   constexpr int NQB = BQ / 32, NDB = D / 32, NT16 = D / 16;
@@ -721,6 +901,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void dkv_bf16_kernel(KArgs a) {
   __shared__ int sSeg[2][BQ];
   __shared__ unsigned char sFlag[MAX_TILES];
   __shared__ unsigned char sMixed[MAX_TILES];
+  __shared__ unsigned char sFlag2[WDS ? MAX_TILES : 1];
   __shared__ int sRange[2];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -762,11 +943,12 @@ __global__ __launch_bounds__(NTHREADS, 1) void dkv_bf16_kernel(KArgs a) {
 
   int t_lo = 0, t_hi = 0;
   const bool any = query_tile_range(k0, k1, BQ, ms, &t_lo, &t_hi);
-  if (has_seg && any) segment_flags(segb, k0, k1, t_lo, t_hi, BQ, L, tid, sFlag, sMixed, sRange);
+  if (has_seg && any)
+    segment_flags(segb, k0, k1, t_lo, t_hi, BQ, L, tid, sFlag, sMixed, sRange, WDS ? sFlag2 : nullptr);
   auto next_needed = [&](int t) -> int {
     for (; t < t_hi; ++t) {
       if (tile_class(t * BQ, t * BQ + BQ, k0, k1, ms) == TILE_EMPTY) continue;
-      if (has_seg && !sFlag[t - t_lo]) continue;
+      if (has_seg && !(sFlag[t - t_lo] && (!WDS || sFlag2[t - t_lo]))) continue;
       return t;
     }
     return -1;
@@ -854,6 +1036,25 @@ __global__ __launch_bounds__(NTHREADS, 1) void dkv_bf16_kernel(KArgs a) {
 #pragma unroll
   for (int i = 0; i < NDB; ++i) dkacc[i] = dvacc[i] = f32x16{};
 
+  // Stored dS: lane (key kw0 + l32, half hh) holds, for query block qb, the
+  // queries 32 qb + 16 h + 8 hh + 0..7 in its dS operand hi[h] (h = 0, 1):
+  // two 16-byte runs of its key's row of the key-major tile.
+  const DsBand band = ds_band(L, a.causal, a.window);
+  const long ds_lane = (long)(wave * 32 + l32) * DS_T + 8 * hh;
+  auto ds_row = [&](int g, int t) -> bf16* {
+    if (!WDS) return nullptr;
+    const long long slot = ds_slot(t, kt, band);
+    if (slot < 0) return nullptr;
+    const long long head = (long long)b * a.Hq + hkv * G + g;
+    return (bf16*)a.ds + (head * a.ds_slots + slot) * DS_ELEMS + ds_lane;
+  };
+  auto store_ds = [&](bf16* row, int qb, const bf16x8 (&hi)[2]) {
+    if (WDS && row != nullptr) {
+      *(bf16x8*)(row + 32 * qb) = hi[0];
+      *(bf16x8*)(row + 32 * qb + 16) = hi[1];
+    }
+  };
+
   int gc = 0, tc = any ? next_needed(t_lo) : -1;
   bool have = tc >= 0;
   if (have) {
@@ -874,6 +1075,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void dkv_bf16_kernel(KArgs a) {
       tn = tc;
     }
     const int q0 = tc * BQ;
+    bf16* const dsrow = ds_row(gc, tc);
     const char* Qt = sQ[stg];
     const char* Ot = sO[stg];
     // the tile class is the same on every lane; readfirstlane lets the compiler
@@ -965,6 +1167,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void dkv_bf16_kernel(KArgs a) {
     elementwise(s0, p0, 0);
     bf16x8 pbp[2], hip[2], lop[2];   // P and dS of the previous block
     pack(s0[0], p0[0], pbp, hip, lop);
+    store_ds(dsrow, 0, hip);
     // Blocks 1 ..: each block's S / dP with the previous block's dV / dK
     // between them (~10 independent MFMA chains in flight; only one block's
     // S / dP accumulators live), then its element work.
@@ -1000,6 +1203,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void dkv_bf16_kernel(KArgs a) {
       }
       elementwise(s1, p1, qb);
       pack(s1[0], p1[0], pbp, hip, lop);
+      store_ds(dsrow, qb, hip);
     }
     // the last block's dV / dK
     {
@@ -1076,14 +1280,14 @@ static void dq_bf16_d(const KArgs& a, int cap, hipStream_t s) {
   }
 }
 
-template <int D, bool P>
+template <int D, bool P, bool W = false>
 static void dkv_bf16_d(const KArgs& a, int cap, hipStream_t s) {
   dim3 grid(a.n_items), block(NTHREADS);
   switch (cap) {
-    case 0: hipLaunchKernelGGL((dkv_bf16_kernel<D, 0, P>), grid, block, 0, s, a); break;
-    case 1: hipLaunchKernelGGL((dkv_bf16_kernel<D, 1, P>), grid, block, 0, s, a); break;
-    case 2: hipLaunchKernelGGL((dkv_bf16_kernel<D, 2, P>), grid, block, 0, s, a); break;
-    default: hipLaunchKernelGGL((dkv_bf16_kernel<D, 3, P>), grid, block, 0, s, a); break;
+    case 0: hipLaunchKernelGGL((dkv_bf16_kernel<D, 0, P, W>), grid, block, 0, s, a); break;
+    case 1: hipLaunchKernelGGL((dkv_bf16_kernel<D, 1, P, W>), grid, block, 0, s, a); break;
+    case 2: hipLaunchKernelGGL((dkv_bf16_kernel<D, 2, P, W>), grid, block, 0, s, a); break;
+    default: hipLaunchKernelGGL((dkv_bf16_kernel<D, 3, P, W>), grid, block, 0, s, a); break;
   }
 }
 
@@ -1105,6 +1309,19 @@ hipError_t launch_dkv_bf16(const KArgs& a, int head_dim, int cap, hipStream_t s)
   const bool p = a.precise_ds != 0;
   if (head_dim == 64) p ? dkv_bf16_d<64, true>(a, cap, s) : dkv_bf16_d<64, false>(a, cap, s);
   else p ? dkv_bf16_d<128, true>(a, cap, s) : dkv_bf16_d<128, false>(a, cap, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_dkv_ds_bf16(const KArgs& a, int head_dim, int cap, hipStream_t s) {
+  if (head_dim == 64) dkv_bf16_d<64, false, true>(a, cap, s);
+  else dkv_bf16_d<128, false, true>(a, cap, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_dq_ds_bf16(const KArgs& a, int head_dim, hipStream_t s) {
+  dim3 grid(a.n_items), block(NTHREADS);
+  if (head_dim == 64) hipLaunchKernelGGL((dq_ds_bf16_kernel<64>), grid, block, 0, s, a);
+  else hipLaunchKernelGGL((dq_ds_bf16_kernel<128>), grid, block, 0, s, a);
   return hipGetLastError();
 }
 

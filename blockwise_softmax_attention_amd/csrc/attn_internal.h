@@ -53,6 +53,10 @@ struct KArgs {
   int n_items;             // workgroups doing real work
   int n_q_tiles;           // ceil(L / BM)
   int n_kv_tiles;          // ceil(L / BKV)
+  // Stored-dS backward: bf16 dS tiles (see DS_T in attn_tiles.h), written by
+  // the dK/dV kernel and read by the dQ kernel of that path.
+  void* ds;
+  long long ds_slots;      // tiles per (batch row, query head)
 };
 
 // Launchers (one per kernel family); dtype 0 = f32, 1 = bf16; cap 0..3.
@@ -68,5 +72,9 @@ int fwd_key_tile(int dtype, int head_dim);   // keys per forward tile
 hipError_t launch_fwd_bf16(const KArgs& a, int head_dim, int cap, hipStream_t s);
 hipError_t launch_dq_bf16(const KArgs& a, int head_dim, int cap, hipStream_t s);
 hipError_t launch_dkv_bf16(const KArgs& a, int head_dim, int cap, hipStream_t s);
+// stored-dS backward (bf16, single-bf16 dS): dK/dV that also writes a.ds, and
+// dQ = dS K from it
+hipError_t launch_dkv_ds_bf16(const KArgs& a, int head_dim, int cap, hipStream_t s);
+hipError_t launch_dq_ds_bf16(const KArgs& a, int head_dim, hipStream_t s);
 
 }  // namespace attn

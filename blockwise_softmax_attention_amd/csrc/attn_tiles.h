@@ -119,3 +119,47 @@ ATTN_HD bool query_tile_range(int k0, int k1, int bm, const MaskSpec& s, int* t0
 }
 
 }  // namespace attn
+
+namespace attn {
+
+// Stored dS tiles.  The stored-dS backward keeps dS (bf16) of every visited
+// block of DS_T queries x DS_T keys, key-major (256 bytes per key for
+// DS_T = 128), so the dQ contraction can read it instead of recomputing it.
+// Query tile qt of one (batch row, query head) owns the slots of its key-tile
+// band [ds_lo(qt), ds_hi(qt)), the key_tile_range of causal and window bounds
+// (identical for every batch row and head: ranker and segment skips only
+// leave slots unused), packed one query tile after another.
+constexpr int DS_T = 128;
+constexpr int DS_ELEMS = DS_T * DS_T;
+
+struct DsBand {
+  int nt;       // tiles per side, ceil(L / DS_T)
+  int causal;
+  int c;        // window: band reaches c tiles below the diagonal (nt when off)
+};
+
+ATTN_HD DsBand ds_band(int L, int causal, int window) {
+  DsBand d;
+  d.nt = (L + DS_T - 1) / DS_T;
+  d.causal = causal;
+  // first key of row q0 = DS_T qt is q0 - W + 1, in tile qt - ceil((W - 1) / DS_T)
+  d.c = window > 0 ? (window + DS_T - 2) / DS_T : d.nt;
+  return d;
+}
+ATTN_HD int ds_lo(int qt, const DsBand& d) { return imax(0, qt - d.c); }
+ATTN_HD int ds_hi(int qt, const DsBand& d) { return d.causal ? qt + 1 : d.nt; }
+// First slot of query tile qt: sum over earlier query tiles of the band widths.
+ATTN_HD long long ds_offset(int qt, const DsBand& d) {
+  const long long q = qt;
+  const long long his = d.causal ? q * (q + 1) / 2 : q * d.nt;
+  const long long n = q - 1 - d.c > 0 ? q - 1 - d.c : 0;   // rows with ds_lo > 0
+  return his - n * (n + 1) / 2;
+}
+ATTN_HD long long ds_slots_per_head(const DsBand& d) { return ds_offset(d.nt, d); }
+// Slot of block (qt, kt), or -1 outside the band.
+ATTN_HD long long ds_slot(int qt, int kt, const DsBand& d) {
+  if (kt < ds_lo(qt, d) || kt >= ds_hi(qt, d)) return -1;
+  return ds_offset(qt, d) + (kt - ds_lo(qt, d));
+}
+
+}  // namespace attn

@@ -159,6 +159,40 @@ attn_status attn_bwd_dkv(const attn_params* params, const void* q, const void* k
                          const float* l, const float* delta, float* dk, float* dv,
                          void* stream);
 
+/* Stored-dS backward: the same dQ, dK, dV as attn_bwd_dq + attn_bwd_dkv
+ * (triton_kernels.py page, dq and dkv kernels; the chain of the
+ * mosaic_backward.py page's module docstring), with dS computed once.
+ * attn_bwd_dkv_ds does the work of attn_bwd_dkv and also stores dS, rounded
+ * to bfloat16 exactly as it enters the dK product, into the caller's
+ * workspace `ds`; attn_bwd_dq_ds then forms dQ = dS K from it, with no
+ * recomputation of S, P or dP.  Call them in that order on one stream; the
+ * workspace holds no state beyond that pair of calls and may be reused.
+ *
+ * Requirements: params.dtype == ATTN_BF16 (else ATTN_ERR_DTYPE) and
+ * params.precise_ds == 0 (else ATTN_ERR_UNSUPPORTED: the stored dS is a single
+ * bf16; with precise_ds use attn_bwd_dq, whose dS enters as hi + lo).
+ *
+ * Workspace: device memory of attn_bwd_ds_workspace_size() bytes, 16-byte
+ * aligned, owned by the caller.  Layout (opaque to callers): per (batch row,
+ * query head), one 128 x 128 bf16 tile (key-major) per block of 128 queries x
+ * 128 keys inside the causal / window band of its query block; blocks with
+ * no visible pair are neither written nor read.  Size: B * Hq * tiles * 32 KiB
+ * with tiles = T (T + 1) / 2 for causal attention without a window,
+ * T = ceil(L / 128) (about L^2 bytes per head), T^2 without a mask, and about
+ * T (W / 128 + 2) with a window W.
+ *
+ * attn_bwd_dq_ds reads only k, segment_ids, ranker_bounds and ds (the same
+ * segment ids and ranker bounds as the attn_bwd_dkv_ds call that wrote ds)
+ * and writes dq (B, L, Hq, D) float. */
+attn_status attn_bwd_ds_workspace_size(const attn_params* params, uint64_t* bytes);
+attn_status attn_bwd_dkv_ds(const attn_params* params, const void* q, const void* k, const void* v,
+                            const float* temperature, const int32_t* segment_ids,
+                            const int32_t* ranker_bounds, const void* d_o, const float* m,
+                            const float* l, const float* delta, float* dk, float* dv, void* ds,
+                            void* stream);
+attn_status attn_bwd_dq_ds(const attn_params* params, const void* k, const int32_t* segment_ids,
+                           const int32_t* ranker_bounds, const void* ds, float* dq, void* stream);
+
 /* Host only, no GPU needed: exact number of visible (query, key) pairs summed
  * over batch rows and query heads, and the number of (query tile, key tile)
  * pairs the forward kernel visits, summed likewise.  segment_ids_host and

@@ -186,3 +186,69 @@ def test_plan_count_closed_forms_of_workloads():
     rb = np.array([[0, 5000, 5000, 8192], [0, 4096, 4096, 8192]], dtype=np.int32)
     p = ba.AttnParams(batch=2, seq_len=8192, q_heads=16, kv_heads=4, head_dim=128)
     assert ba.attn_plan_count(p, None, rb)[0] == 16 * sum(8192 * h + 8192 - h for h in (5000, 4096))
+
+
+# ---------------------------------------------------------------------------
+# Stored-dS workspace: size and requirements (host only)
+# ---------------------------------------------------------------------------
+
+def brute_ds_tiles(L, causal, window, T=128):
+    """Per (batch row, head): sum over query tiles of the width of the key-tile
+    band between the first and last key any of its rows may see under the
+    causal and window predicates (segments and ranker bounds left aside)."""
+    nt = (L + T - 1) // T
+    total = 0
+    for qt in range(nt):
+        rows = np.arange(qt * T, min(qt * T + T, L))
+        keys = np.arange(L)
+        vis = np.ones((rows.size, L), dtype=bool)
+        if causal:
+            vis &= keys[None, :] <= rows[:, None]
+        if window > 0:
+            vis &= keys[None, :] > rows[:, None] - window
+        ks = np.nonzero(vis.any(axis=0))[0]
+        assert ks.size > 0
+        total += ks.max() // T - ks.min() // T + 1
+    return total
+
+
+@pytest.mark.parametrize("L", [1, 127, 128, 129, 300, 1000, 2048])
+@pytest.mark.parametrize("causal,window", [(True, 0), (False, 0), (True, 1), (True, 37),
+                                           (True, 128), (True, 129), (True, 257), (False, 200),
+                                           (True, 5000)])
+def test_ds_workspace_size_matches_band(L, causal, window):
+    p = base_params(batch=3, q_heads=4, kv_heads=2, seq_len=L, causal=causal, window_len=window,
+                    precise_ds=False)
+    assert ba.attn_bwd_ds_workspace_size(p) == 3 * 4 * brute_ds_tiles(L, causal, window) * 128 * 128 * 2
+
+
+def test_ds_workspace_closed_forms():
+    # long-context workload: causal, 256 tiles -> 256 * 257 / 2 per head
+    p = base_params(batch=1, q_heads=8, kv_heads=8, seq_len=32768, head_dim=128, precise_ds=False)
+    assert ba.attn_bwd_ds_workspace_size(p) == 8 * (256 * 257 // 2) * 32768
+    # ranker workload: no causal mask -> the full 64 x 64 tiles per head
+    p = base_params(batch=4, q_heads=16, kv_heads=4, seq_len=8192, head_dim=128, causal=False,
+                    precise_ds=False)
+    assert ba.attn_bwd_ds_workspace_size(p) == 64 * 64 * 64 * 32768
+
+
+@pytest.mark.parametrize("kw,status", [(dict(dtype=ba.ATTN_F32), -3), (dict(precise_ds=True), -4)])
+def test_ds_path_requirements(kw, status):
+    d = dict(precise_ds=False)
+    d.update(kw)
+    with pytest.raises(ba.AttnError) as e:
+        ba.attn_bwd_ds_workspace_size(base_params(**d))
+    assert e.value.status == status
+
+
+def test_ds_calls_reject_null_workspace_before_launch():
+    lib = ba.load_library()
+    p = base_params(precise_ds=False)
+    cp = p.to_c()
+    buf = ctypes.create_string_buffer(1 << 16)
+    a = ctypes.addressof(buf)
+    a16 = a + (-a) % 16
+    st = lib.attn_bwd_dq_ds(ctypes.byref(cp), a16, None, None, None, a16, None)
+    assert st == -1 and b"ds" in lib.attn_last_error()
+    st = lib.attn_bwd_dq_ds(ctypes.byref(cp), a16, None, None, a16 + 4, a16, None)
+    assert st == -5

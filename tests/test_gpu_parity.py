@@ -36,12 +36,14 @@ def host_inputs(inp):
                 rb=to_i32(inp["ranker_bounds"]))
 
 
-def run_gpu(w: Workload, inp, precise=True, dtemp=False):
+def run_gpu(w: Workload, inp, precise=True, dtemp=False, stored_ds=None):
+    """Forward and backward through the C ABI; stored_ds None takes the
+    stored-dS backward wherever it applies (bf16, single-bf16 dS, no dtemp)."""
     p = ba.params_for(w, precise)
     dev = {k: (v.cuda() if v is not None else None) for k, v in inp.items()}
     res = ba.attention_forward_backward(p, dev["q"], dev["k"], dev["v"], dev["do"],
                                         dev["temperature"], dev["segment_ids"], dev["ranker_bounds"],
-                                        dtemp=dtemp)
+                                        dtemp=dtemp, stored_ds=stored_ds)
     torch.cuda.synchronize()
     return {k: v.cpu().double().numpy() for k, v in res.items()}
 
@@ -102,7 +104,7 @@ def compare_full(w: Workload, precise=True, groups=None, dtemp=False):
     got = run_gpu(w, inp, precise, dtemp=dtemp)
     if dtemp:
         # the dQ kernel variant that also sums dtemp gives the same dQ, bit for bit
-        plain = run_gpu(w, inp, precise)
+        plain = run_gpu(w, inp, precise, stored_ds=False)
         assert np.array_equal(plain["dq"], got["dq"])
     h = host_inputs(inp)
     ref = backward(h["q"], h["k"], h["v"], h["do"], oracle_params(w), h["temp"], h["seg"], h["rb"],
