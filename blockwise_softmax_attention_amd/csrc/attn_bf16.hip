@@ -54,6 +54,7 @@
 #define ATTN_DKV_PIN 1
 #endif
 
+
 namespace attn {
 
 constexpr int BN16 = ATTN_FWD_BN;   // keys per tile (forward)
@@ -699,28 +700,36 @@ __global__ __launch_bounds__(NTHREADS, 2) void dq_bf16_kernel(KArgs a) {
 // S, P or dP and no element work, so the kernel streams the stored tiles from
 // HBM.  Both operands reduce over keys and are read transposed from LDS
 // (ds_read_b64_tr_b16): the K tile (columns = d) and the key-major dS tile
-// (columns = queries; wave w takes its 32).  NST LDS stages, NST - 1 steps of
-// loads in flight; every step issues the same number of loads (without a
-// further step it refetches its own tiles into the idle stage), so one
-// vmcnt wait finds exactly the loads of the step about to run.
+// (columns = queries; wave w takes its 32).
+//
+// The dS stream is HBM-bound and latency-bound, so it gets the deeper ring:
+// dS of step n + DQS_SST - 1 and K of step n + 2 (K mostly hits L2) are
+// loaded while step n computes.  Every step issues the same loads in the same
+// order (past the last step the last one is fetched again into idle stages),
+// so a single vmcnt wait before the barrier finds both tiles of step n done:
+// the loads issued after K(n) are dS(n+SST-3), K(n+1) and dS(n+SST-2), and
+// dS(n) precedes K(n).
 constexpr int DQS_BN = 64;    // keys per step: half a stored tile
-constexpr int DQS_NST = 4;    // LDS stages
+constexpr int DQS_KST = 3;    // K stages
+constexpr int DQS_SST = 6;    // dS stages
 constexpr int DQS_FLAGS = ATTN_MAX_SEQ_LEN_SEGMENTS / DS_T;
 
 template <int D>
 __global__ __launch_bounds__(NTHREADS, 1) void dq_ds_bf16_kernel(KArgs a) {
-  constexpr int BN = DQS_BN, NST = DQS_NST, HALVES = DS_T / BN;
+  constexpr int BN = DQS_BN, KST = DQS_KST, SST = DQS_SST, HALVES = DS_T / BN;
   using KT = BTile<BN, D, NWAVES>;
   using ST = BTile<BN, DS_T, NWAVES>;
-  constexpr int NDB = D / 32, NDMA = KT::PER_WAVE + ST::PER_WAVE;
+  constexpr int NDB = D / 32, NK = KT::PER_WAVE, NS = ST::PER_WAVE;
   static_assert(BM == DS_T, "a workgroup's query tile is one stored query tile");
+  static_assert(KST == 3 && SST >= 4, "load order of the two rings");
 
-  __shared__ __attribute__((aligned(1024))) char sK[NST][KT::BYTES];
-  __shared__ __attribute__((aligned(1024))) char sS[NST][ST::BYTES];
+  __shared__ __attribute__((aligned(1024))) char sK[KST][KT::BYTES];
+  __shared__ __attribute__((aligned(1024))) char sS[SST][ST::BYTES];
   __shared__ unsigned char sFlag[DQS_FLAGS];
   __shared__ unsigned char sFlag2[DQS_FLAGS];
   __shared__ unsigned char sMixed[DQS_FLAGS];
-  __shared__ int sRange[2];
+  __shared__ unsigned short sList[ATTN_MAX_SEQ_LEN / DS_T];   // visited key tiles - t_lo
+  __shared__ int sRange[3];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -747,94 +756,79 @@ __global__ __launch_bounds__(NTHREADS, 1) void dq_ds_bf16_kernel(KArgs a) {
   const int* segb = has_seg ? a.seg + (long)b * L : nullptr;
   if (has_seg)
     segment_flags(segb, it.q0, it.q1, t_lo, t_hi, DS_T, L, tid, sFlag, sMixed, sRange, sFlag2);
-  // the blocks the dK/dV kernel visited (and stored): the same tile class and
-  // symmetric segment test, evaluated from the query side
-  auto next_tile = [&](int t) -> int {
-    for (; t < t_hi; ++t) {
-      if (tile_class(it.q0, it.q1, t * DS_T, t * DS_T + DS_T, ms) == TILE_EMPTY) continue;
-      if (has_seg && !(sFlag[t - t_lo] && sFlag2[t - t_lo])) continue;
-      return t;
+  // The blocks the dK/dV kernel visited (and stored): the same tile class and
+  // symmetric segment test, evaluated from the query side once, by wave 0,
+  // into a compact list of key tiles (the loop then only indexes it).
+  if (wave == 0) {
+    int cnt = 0;
+    for (int t0 = t_lo; t0 < t_hi; t0 += 64) {
+      const int t = t0 + lane;
+      bool vis = t < t_hi &&
+                 tile_class(it.q0, it.q1, t * DS_T, t * DS_T + DS_T, ms) != TILE_EMPTY;
+      if (vis && has_seg) vis = sFlag[t - t_lo] && sFlag2[t - t_lo];
+      const uint64_t m = __ballot(vis);
+      const int pos = cnt + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                           __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
+      if (vis) sList[pos] = (unsigned short)(t - t_lo);
+      cnt += __builtin_popcountll(m);
     }
-    return -1;
-  };
-  // steps: (key tile, half) with the half's first key inside the sequence;
-  // kt >= 0 on entry, -1 on return after the last step
-  auto next_step = [&](int& kt, int& hf) {
-    if (hf + 1 < HALVES && kt * DS_T + (hf + 1) * BN < L) {
-      ++hf;
-      return;
-    }
-    kt = next_tile(kt + 1);
-    hf = 0;
-  };
-  auto issue_one = [&](int kt, int hf, int stg, int i) {
-    const int kr0 = kt * DS_T + hf * BN;
-    if (i < KT::PER_WAVE) {
-      KT::issue_one(lds_offset(sK[stg]), Kb + (long)kr0 * kv_rs, kv_rsb, L - kr0, kln, wave, i);
-    } else {
-      ST::issue_one(lds_offset(sS[stg]), Sb + ((long)(kt - t_lo) * DS_ELEMS + (long)hf * BN * DS_T),
-                    S_RSB, BN, sln, wave, i - KT::PER_WAVE);
-    }
-  };
-  auto issue = [&](int kt, int hf, int stg) {
+    if (lane == 0) sRange[2] = cnt;
+  }
+  __syncthreads();
+  const int ntiles = sRange[2];
+  // a step is one half of a listed tile; the second half of the sequence's
+  // last tile is dropped when it starts at or past L
+  const int last = ntiles > 0 ? t_lo + sList[ntiles - 1] : 0;
+  const int nsteps = 2 * ntiles - ((ntiles > 0 && last * DS_T + BN >= L) ? 1 : 0);
+  auto issue_k = [&](int n, int stg) {
+    const int kt = t_lo + sList[n >> 1];
+    const int kr0 = kt * DS_T + (n & 1) * BN;
 #pragma unroll
-    for (int i = 0; i < NDMA; ++i) issue_one(kt, hf, stg, i);
+    for (int i = 0; i < NK; ++i)
+      KT::issue_one(lds_offset(sK[stg]), Kb + (long)kr0 * kv_rs, kv_rsb, L - kr0, kln, wave, i);
+  };
+  auto issue_s = [&](int n, int stg) {
+    const bf16* g = Sb + ((long)sList[n >> 1] * DS_ELEMS + (long)(n & 1) * BN * DS_T);
+#pragma unroll
+    for (int i = 0; i < NS; ++i) ST::issue_one(lds_offset(sS[stg]), g, S_RSB, BN, sln, wave, i);
   };
 
   f32x16 dqacc[NDB];
 #pragma unroll
   for (int i = 0; i < NDB; ++i) dqacc[i] = f32x16{};
 
-  // prologue: steps 0 .. NST-2 into stages 0 .. NST-2 (the last real step
-  // repeated where there are fewer)
-  int ck = next_tile(t_lo), ch = 0;
-  int lk = ck, lh = ch;   // last step issued
-  if (ck >= 0) {
-    issue(ck, ch, 0);
+  if (nsteps > 0) {
+    // prologue: dS(0 .. SST-4), K(0), dS(SST-3), K(1), dS(SST-2); step
+    // numbers past the last step repeat the last one
+    const int nl = nsteps - 1;
 #pragma unroll
-    for (int s = 1; s < NST - 1; ++s) {
-      int nk = lk, nh = lh;
-      next_step(nk, nh);
-      if (nk >= 0) {
-        lk = nk;
-        lh = nh;
+    for (int n = 0; n < SST - 3; ++n) issue_s(imin(n, nl), n);
+    issue_k(0, 0);
+    issue_s(imin(SST - 3, nl), SST - 3);
+    issue_k(imin(1, nl), 1);
+    issue_s(imin(SST - 2, nl), SST - 2);
+    int ks = 0, ss = 0;   // stages of the current step
+    for (int n = 0; n < nsteps; ++n) {
+      wait_vmcnt<2 * NS + NK>();
+      __syncthreads();
+      issue_k(imin(n + 2, nl), ks == 0 ? 2 : ks - 1);
+      issue_s(imin(n + SST - 1, nl), ss == 0 ? SST - 1 : ss - 1);
+      const char* Kt = sK[ks];
+      const char* St = sS[ss];
+#pragma unroll
+      for (int t = 0; t < BN / 16; ++t) {
+        const bf16x8 sf = ST::tr_frag(St, wave, t, lane);
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          const bf16x8 ka = KT::tr_frag(Kt, db, t, lane);
+          dqacc[db] = Elem<bf16>::mfma(ka, sf, dqacc[db]);
+        }
       }
-      issue(lk, lh, s);
+      ks = ks + 1 == KST ? 0 : ks + 1;
+      ss = ss + 1 == SST ? 0 : ss + 1;
     }
+    wait_vmcnt<0>();
   }
-  int fk = lk, fh = lh;   // frontier: the next step to issue follows it
-  bool fdone = false;
-  int stg = 0;
-  while (ck >= 0) {
-    wait_vmcnt<NDMA * (NST - 2)>();
-    __syncthreads();
-    // loads of step + NST - 1 into the stage freed by the previous step
-    {
-      int nk = fk, nh = fh;
-      if (!fdone) next_step(nk, nh);
-      if (nk >= 0 && !fdone) {
-        fk = nk;
-        fh = nh;
-      } else {
-        fdone = true;
-      }
-      issue(fk, fh, (stg + NST - 1) % NST);
-    }
-    const char* Kt = sK[stg];
-    const char* St = sS[stg];
-#pragma unroll
-    for (int t = 0; t < BN / 16; ++t) {
-      const bf16x8 sf = ST::tr_frag(St, wave, t, lane);
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        const bf16x8 ka = KT::tr_frag(Kt, db, t, lane);
-        dqacc[db] = Elem<bf16>::mfma(ka, sf, dqacc[db]);
-      }
-    }
-    next_step(ck, ch);
-    stg = (stg + 1) % NST;
-  }
-  wait_vmcnt<0>();
 
   if (qrow < L) {
     float* drow = a.out0 + ((long)(b * L + qrow) * a.Hq + it.hq) * D;

@@ -61,21 +61,30 @@ template <> struct Elem<bf16> {
   }
   __device__ __forceinline__ static frag load(const bf16* p) { return *(const frag*)p; }
   __device__ __forceinline__ static frag zero() { return frag{}; }
+  // Two floats rounded to bf16 (RNE) as one packed pair: one
+  // v_cvt_pk_bf16_f32 (element-wise casts become one conversion per value
+  // plus a v_perm_b32 per pair).
+  __device__ __forceinline__ static uint32_t pack2(float a, float b) {
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, bf16x2));
+  }
   // Eight consecutive C registers starting at r0, rounded to bf16 (RNE).
   __device__ __forceinline__ static frag from_acc(const f32x16& c, int r0) {
-    frag f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) f[i] = (bf16)c[r0 + i];
-    return f;
+    uint4 w;
+    w.x = pack2(c[r0 + 0], c[r0 + 1]);
+    w.y = pack2(c[r0 + 2], c[r0 + 3]);
+    w.z = pack2(c[r0 + 4], c[r0 + 5]);
+    w.w = pack2(c[r0 + 6], c[r0 + 7]);
+    return __builtin_bit_cast(frag, w);
   }
   // hi + lo split: lo carries the rounding error of hi.
   __device__ __forceinline__ static void split_acc(const f32x16& c, int r0, frag& hi, frag& lo) {
+    hi = from_acc(c, r0);
+    f32x16 r;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      bf16 x = (bf16)c[r0 + i];
-      hi[i] = x;
-      lo[i] = (bf16)(c[r0 + i] - (float)x);
-    }
+    for (int i = 0; i < 8; ++i) r[r0 + i] = c[r0 + i] - (float)hi[i];
+    lo = from_acc(r, r0);
   }
 };
 
