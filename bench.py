@@ -27,17 +27,23 @@ PEAK_F32_TFLOPS = 157.3        # fp32 (matrix and vector)
 HBM_GBPS = 8000.0
 
 # HBM bytes per launch measured with rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE on the
-# long-context workload, scaled by what the same counters read for a plain 1 GiB
-# device copy (FETCH_SIZE x2.0, WRITE_SIZE x1.0); keyed by a hash of the kernel
+# long-context and ranker workloads (default mode: single-bf16 dS, stored-dS
+# backward), scaled by what the same counters read for a plain 1 GiB device
+# copy (FETCH_SIZE x2.0, WRITE_SIZE x1.0); keyed by a hash of the kernel
 # sources they were taken on, so a changed kernel reports null.  Summary and
-# commands: profiles/counters_long_context_causal_alsc_L32768.md.
+# commands: profiles/counters_long_context_causal_alsc_L32768.md and
+# profiles/kernel_trace_ranker_gqa_softsign_L8192.md.
 KERNEL_SOURCES = ["attn_bf16.hip", "attn_bf16.h", "attn_device.h", "attn_tiles.h",
                   "attn_internal.h", "attn_bwd_common.h", "attn_preprocess.hip"]
 MEASURED_TRAFFIC = {
-    ("5c5cd5bb99faef25", 5, 0): {"attn_fwd": (234737 * 2.0 + 133823) * 1024,
+    ("23d843e0afdaf301", 5, 0): {"attn_fwd": (241410 * 2.0 + 134079) * 1024,
                                  "attn_bwd_preprocess": (98333 * 2.0 + 4097) * 1024,
-                                 "attn_bwd_dq": (268297 * 2.0 + 131073) * 1024,
-                                 "attn_bwd_dkv": (361814 * 2.0 + 262144) * 1024},
+                                 "attn_bwd_dkv_ds": (629358 * 2.0 + 8712941) * 1024,
+                                 "attn_bwd_dq_ds": (4453005 * 2.0 + 131072) * 1024},
+    ("23d843e0afdaf301", 4, 0): {"attn_fwd": (553865 * 2.0 + 266292) * 1024,
+                                 "attn_bwd_preprocess": (196637 * 2.0 + 16408) * 1024,
+                                 "attn_bwd_dkv_ds": (1042927 * 2.0 + 6423375) * 1024,
+                                 "attn_bwd_dq_ds": (3585582 * 2.0 + 262144) * 1024},
 }
 
 
