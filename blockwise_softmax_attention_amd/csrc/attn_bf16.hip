@@ -709,14 +709,20 @@ __global__ __launch_bounds__(NTHREADS, 2) void dq_bf16_kernel(KArgs a) {
 // so a single vmcnt wait before the barrier finds both tiles of step n done:
 // the loads issued after K(n) are dS(n+SST-3), K(n+1) and dS(n+SST-2), and
 // dS(n) precedes K(n).
-constexpr int DQS_BN = 64;    // keys per step: half a stored tile
-constexpr int DQS_KST = 3;    // K stages
-constexpr int DQS_SST = 6;    // dS stages
+#ifndef ATTN_DQS_BN
+#define ATTN_DQS_BN 32
+#endif
+constexpr int DQS_BN = ATTN_DQS_BN;               // keys per step (a part of a stored tile)
+constexpr int DQS_KST = 3;                        // K stages
+constexpr int DQS_SST = DQS_BN == 32 ? 5 : 6;     // dS stages
+constexpr int DQS_WG_PER_CU = DQS_BN == 32 ? 2 : 1;
 constexpr int DQS_FLAGS = ATTN_MAX_SEQ_LEN_SEGMENTS / DS_T;
 
 template <int D>
-__global__ __launch_bounds__(NTHREADS, 1) void dq_ds_bf16_kernel(KArgs a) {
-  constexpr int BN = DQS_BN, KST = DQS_KST, SST = DQS_SST, HALVES = DS_T / BN;
+__global__ __launch_bounds__(NTHREADS, DQS_WG_PER_CU) void dq_ds_bf16_kernel(KArgs a) {
+  constexpr int BN = DQS_BN, KST = DQS_KST, SST = DQS_SST, PARTS = DS_T / BN;
+  constexpr int PSH = PARTS == 4 ? 2 : 1;   // log2(PARTS)
+  static_assert(PARTS == 2 || PARTS == 4, "a stored tile splits into 2 or 4 steps");
   using KT = BTile<BN, D, NWAVES>;
   using ST = BTile<BN, DS_T, NWAVES>;
   constexpr int NDB = D / 32, NK = KT::PER_WAVE, NS = ST::PER_WAVE;
@@ -776,19 +782,20 @@ __global__ __launch_bounds__(NTHREADS, 1) void dq_ds_bf16_kernel(KArgs a) {
   }
   __syncthreads();
   const int ntiles = sRange[2];
-  // a step is one half of a listed tile; the second half of the sequence's
-  // last tile is dropped when it starts at or past L
+  // a step is one BN-key part of a listed tile; the parts of the sequence's
+  // last tile that start at or past L are dropped
   const int last = ntiles > 0 ? t_lo + sList[ntiles - 1] : 0;
-  const int nsteps = 2 * ntiles - ((ntiles > 0 && last * DS_T + BN >= L) ? 1 : 0);
+  const int last_parts = imin(PARTS, (L - last * DS_T + BN - 1) / BN);
+  const int nsteps = ntiles > 0 ? PARTS * (ntiles - 1) + last_parts : 0;
   auto issue_k = [&](int n, int stg) {
-    const int kt = t_lo + sList[n >> 1];
-    const int kr0 = kt * DS_T + (n & 1) * BN;
+    const int kt = t_lo + sList[n >> PSH];
+    const int kr0 = kt * DS_T + (n & (PARTS - 1)) * BN;
 #pragma unroll
     for (int i = 0; i < NK; ++i)
       KT::issue_one(lds_offset(sK[stg]), Kb + (long)kr0 * kv_rs, kv_rsb, L - kr0, kln, wave, i);
   };
   auto issue_s = [&](int n, int stg) {
-    const bf16* g = Sb + ((long)sList[n >> 1] * DS_ELEMS + (long)(n & 1) * BN * DS_T);
+    const bf16* g = Sb + ((long)sList[n >> PSH] * DS_ELEMS + (long)(n & (PARTS - 1)) * BN * DS_T);
 #pragma unroll
     for (int i = 0; i < NS; ++i) ST::issue_one(lds_offset(sS[stg]), g, S_RSB, BN, sln, wave, i);
   };
