@@ -36,14 +36,14 @@ HBM_GBPS = 8000.0
 KERNEL_SOURCES = ["attn_bf16.hip", "attn_bf16.h", "attn_device.h", "attn_tiles.h",
                   "attn_internal.h", "attn_bwd_common.h", "attn_preprocess.hip"]
 MEASURED_TRAFFIC = {
-    ("23d843e0afdaf301", 5, 0): {"attn_fwd": (241410 * 2.0 + 134079) * 1024,
+    ("44fc00a01f89aae5", 5, 0): {"attn_fwd": (239660 * 2.0 + 133984) * 1024,
                                  "attn_bwd_preprocess": (98333 * 2.0 + 4097) * 1024,
-                                 "attn_bwd_dkv_ds": (629358 * 2.0 + 8712941) * 1024,
-                                 "attn_bwd_dq_ds": (4453005 * 2.0 + 131072) * 1024},
-    ("23d843e0afdaf301", 4, 0): {"attn_fwd": (553865 * 2.0 + 266292) * 1024,
-                                 "attn_bwd_preprocess": (196637 * 2.0 + 16408) * 1024,
-                                 "attn_bwd_dkv_ds": (1042927 * 2.0 + 6423375) * 1024,
-                                 "attn_bwd_dq_ds": (3585582 * 2.0 + 262144) * 1024},
+                                 "attn_bwd_dkv_ds": (619389 * 2.0 + 8713805) * 1024,
+                                 "attn_bwd_dq_ds": (4696666 * 2.0 + 131120) * 1024},
+    ("44fc00a01f89aae5", 4, 0): {"attn_fwd": (548384 * 2.0 + 266295) * 1024,
+                                 "attn_bwd_preprocess": (196638 * 2.0 + 16409) * 1024,
+                                 "attn_bwd_dkv_ds": (1051513 * 2.0 + 6423406) * 1024,
+                                 "attn_bwd_dq_ds": (3728650 * 2.0 + 262167) * 1024},
 }
 
 
