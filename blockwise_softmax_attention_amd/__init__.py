@@ -84,8 +84,8 @@ _FN_SIGS = {
     "attn_check_params": [ctypes.POINTER(_CParams)],
     "attn_bwd_ds_workspace_size": [ctypes.POINTER(_CParams), ctypes.POINTER(ctypes.c_uint64)],
     "attn_bwd_dkv_ds": [ctypes.POINTER(_CParams), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
-                        _P],
-    "attn_bwd_dq_ds": [ctypes.POINTER(_CParams), _P, _P, _P, _P, _P, _P],
+                        ctypes.c_uint64, _P],
+    "attn_bwd_dq_ds": [ctypes.POINTER(_CParams), _P, _P, _P, _P, ctypes.c_uint64, _P, _P],
 }
 
 
@@ -253,7 +253,7 @@ def attn_bwd_dkv_ds(p: AttnParams, q, k, v, d_o, m, l, delta, ds, temperature=No
         _ptr(ranker_bounds, "ranker_bounds", torch.int32), _ptr(d_o, "d_o", dt),
         _ptr(m, "m", torch.float32), _ptr(l, "l", torch.float32), _ptr(delta, "delta", torch.float32),
         _ptr(dk, "dk", torch.float32), _ptr(dv, "dv", torch.float32), _ptr(ds, "ds", torch.uint8),
-        _stream(stream)))
+        int(ds.numel()), _stream(stream)))
     return dk, dv
 
 
@@ -265,7 +265,7 @@ def attn_bwd_dq_ds(p: AttnParams, k, ds, segment_ids=None, ranker_bounds=None, d
     _check(load_library().attn_bwd_dq_ds(
         ctypes.byref(cp), _ptr(k, "k", _in_dtype(p)), _ptr(segment_ids, "segment_ids", torch.int32),
         _ptr(ranker_bounds, "ranker_bounds", torch.int32), _ptr(ds, "ds", torch.uint8),
-        _ptr(dq, "dq", torch.float32), _stream(stream)))
+        int(ds.numel()), _ptr(dq, "dq", torch.float32), _stream(stream)))
     return dq
 
 
@@ -298,11 +298,13 @@ def attn_plan_count(p: AttnParams, segment_ids=None, ranker_bounds=None):
 
 def attention_forward_backward(p: AttnParams, q, k, v, d_o, temperature=None, segment_ids=None,
                                ranker_bounds=None, dtemp: bool = False, stream=None,
-                               stored_ds: Optional[bool] = None):
+                               stored_ds: Optional[bool] = None, ds=None):
     """One pass of the whole path: forward, then preprocess, dQ and dK/dV
     (and, with dtemp=True, the temperature gradient (B, L)).  stored_ds: use
     the stored-dS backward (dK/dV, then dQ from the stored dS); None picks it
-    whenever it applies (stored_ds_eligible)."""
+    whenever it applies (stored_ds_eligible).  ds: a workspace to reuse
+    (uint8, at least attn_bwd_ds_workspace_size bytes); one is allocated if
+    not given."""
     o, m, l = attn_fwd(p, q, k, v, temperature, segment_ids, ranker_bounds, stream=stream)
     delta = attn_bwd_preprocess(p, o, d_o, stream=stream)
     if stored_ds is None:
@@ -310,7 +312,8 @@ def attention_forward_backward(p: AttnParams, q, k, v, d_o, temperature=None, se
     if stored_ds:
         if dtemp:
             raise ValueError("the temperature gradient needs the recomputing dQ (stored_ds=False)")
-        ds = ds_workspace(p, q.device)
+        if ds is None:
+            ds = ds_workspace(p, q.device)
         dk, dv = attn_bwd_dkv_ds(p, q, k, v, d_o, m, l, delta, ds, temperature, segment_ids,
                                  ranker_bounds, stream=stream)
         dq = attn_bwd_dq_ds(p, k, ds, segment_ids, ranker_bounds, stream=stream)

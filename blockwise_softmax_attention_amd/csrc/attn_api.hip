@@ -315,16 +315,26 @@ attn_status attn_bwd_ds_workspace_size(const attn_params* p, uint64_t* bytes) {
   return ATTN_OK;
 }
 
+static attn_status check_ds_workspace(const attn_params* p, const void* ds, uint64_t ds_bytes) {
+  ATTN_TRY(check_ptr(ds, "ds", 16));
+  uint64_t need = 0;
+  ATTN_TRY(attn_bwd_ds_workspace_size(p, &need));
+  if (ds_bytes < need)
+    return fail(ATTN_ERR_SHAPE, "ds workspace of " + std::to_string(ds_bytes) + " bytes, " +
+                                    std::to_string(need) + " needed");
+  return ATTN_OK;
+}
+
 attn_status attn_bwd_dkv_ds(const attn_params* p, const void* q, const void* k, const void* v,
                             const float* temperature, const int32_t* segment_ids,
                             const int32_t* ranker_bounds, const void* d_o, const float* m,
                             const float* l, const float* delta, float* dk, float* dv, void* ds,
-                            void* stream) {
+                            uint64_t ds_bytes, void* stream) {
   ATTN_TRY(check_ds_params(p));
   ATTN_TRY(check_bwd_inputs(p, q, k, v, temperature, segment_ids, ranker_bounds, d_o, m, l, delta));
   ATTN_TRY(check_ptr(dk, "dk", 16));
   ATTN_TRY(check_ptr(dv, "dv", 16));
-  ATTN_TRY(check_ptr(ds, "ds", 16));
+  ATTN_TRY(check_ds_workspace(p, ds, ds_bytes));
   attn::KArgs a = make_args(p, temperature, segment_ids, ranker_bounds);
   a.q = q;
   a.k = k;
@@ -343,11 +353,12 @@ attn_status attn_bwd_dkv_ds(const attn_params* p, const void* q, const void* k, 
 }
 
 attn_status attn_bwd_dq_ds(const attn_params* p, const void* k, const int32_t* segment_ids,
-                           const int32_t* ranker_bounds, const void* ds, float* dq, void* stream) {
+                           const int32_t* ranker_bounds, const void* ds, uint64_t ds_bytes,
+                           float* dq, void* stream) {
   ATTN_TRY(check_ds_params(p));
   ATTN_TRY(check_common(p, nullptr, segment_ids, ranker_bounds));
   ATTN_TRY(check_ptr(k, "k", 16));
-  ATTN_TRY(check_ptr(ds, "ds", 16));
+  ATTN_TRY(check_ds_workspace(p, ds, ds_bytes));
   ATTN_TRY(check_ptr(dq, "dq", 16));
   attn::KArgs a = make_args(p, nullptr, segment_ids, ranker_bounds);
   a.k = k;

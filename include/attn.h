@@ -181,6 +181,9 @@ attn_status attn_bwd_dkv(const attn_params* params, const void* q, const void* k
  * T = ceil(L / 128) (about L^2 bytes per head), T^2 without a mask, and about
  * T (W / 128 + 2) with a window W.
  *
+ * ds_bytes is the size of the caller's workspace; ATTN_ERR_SHAPE (nothing
+ * launched) if it is smaller than attn_bwd_ds_workspace_size().
+ *
  * attn_bwd_dq_ds reads only k, segment_ids, ranker_bounds and ds (the same
  * segment ids and ranker bounds as the attn_bwd_dkv_ds call that wrote ds)
  * and writes dq (B, L, Hq, D) float. */
@@ -189,9 +192,10 @@ attn_status attn_bwd_dkv_ds(const attn_params* params, const void* q, const void
                             const float* temperature, const int32_t* segment_ids,
                             const int32_t* ranker_bounds, const void* d_o, const float* m,
                             const float* l, const float* delta, float* dk, float* dv, void* ds,
-                            void* stream);
+                            uint64_t ds_bytes, void* stream);
 attn_status attn_bwd_dq_ds(const attn_params* params, const void* k, const int32_t* segment_ids,
-                           const int32_t* ranker_bounds, const void* ds, float* dq, void* stream);
+                           const int32_t* ranker_bounds, const void* ds, uint64_t ds_bytes,
+                           float* dq, void* stream);
 
 /* Host only, no GPU needed: exact number of visible (query, key) pairs summed
  * over batch rows and query heads, and the number of (query tile, key tile)

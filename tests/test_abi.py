@@ -248,7 +248,14 @@ def test_ds_calls_reject_null_workspace_before_launch():
     buf = ctypes.create_string_buffer(1 << 16)
     a = ctypes.addressof(buf)
     a16 = a + (-a) % 16
-    st = lib.attn_bwd_dq_ds(ctypes.byref(cp), a16, None, None, None, a16, None)
+    need = ba.attn_bwd_ds_workspace_size(p)
+    st = lib.attn_bwd_dq_ds(ctypes.byref(cp), a16, None, None, None, need, a16, None)
     assert st == -1 and b"ds" in lib.attn_last_error()
-    st = lib.attn_bwd_dq_ds(ctypes.byref(cp), a16, None, None, a16 + 4, a16, None)
+    st = lib.attn_bwd_dq_ds(ctypes.byref(cp), a16, None, None, a16 + 4, need, a16, None)
     assert st == -5
+    # a workspace smaller than the layout needs is refused before any launch
+    st = lib.attn_bwd_dq_ds(ctypes.byref(cp), a16, None, None, a16, need - 1, a16, None)
+    assert st == -2 and b"needed" in lib.attn_last_error()
+    st = lib.attn_bwd_dkv_ds(ctypes.byref(cp), a16, a16, a16, None, None, None, a16, a16, a16, a16,
+                             a16, a16, a16, need - 1, None)
+    assert st == -2 and b"needed" in lib.attn_last_error()
