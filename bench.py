@@ -36,11 +36,11 @@ HBM_GBPS = 8000.0
 KERNEL_SOURCES = ["attn_bf16.hip", "attn_bf16.h", "attn_device.h", "attn_tiles.h",
                   "attn_internal.h", "attn_bwd_common.h", "attn_preprocess.hip"]
 MEASURED_TRAFFIC = {
-    ("44fc00a01f89aae5", 5, 0): {"attn_fwd": (239660 * 2.0 + 133984) * 1024,
+    ("ee938ed215a19beb", 5, 0): {"attn_fwd": (239660 * 2.0 + 133984) * 1024,
                                  "attn_bwd_preprocess": (98333 * 2.0 + 4097) * 1024,
                                  "attn_bwd_dkv_ds": (619389 * 2.0 + 8713805) * 1024,
                                  "attn_bwd_dq_ds": (4696666 * 2.0 + 131120) * 1024},
-    ("44fc00a01f89aae5", 4, 0): {"attn_fwd": (548384 * 2.0 + 266295) * 1024,
+    ("ee938ed215a19beb", 4, 0): {"attn_fwd": (548384 * 2.0 + 266295) * 1024,
                                  "attn_bwd_preprocess": (196638 * 2.0 + 16409) * 1024,
                                  "attn_bwd_dkv_ds": (1051513 * 2.0 + 6423406) * 1024,
                                  "attn_bwd_dq_ds": (3728650 * 2.0 + 262167) * 1024},
@@ -48,11 +48,17 @@ MEASURED_TRAFFIC = {
 
 
 def kernel_source_hash() -> str:
+    """Hash of the kernel sources' code: comments and whitespace are dropped,
+    so an edited comment keeps the measured traffic, a changed kernel not."""
     import hashlib
+    import re
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "blockwise_softmax_attention_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "blockwise_softmax_attention_amd", "csrc", f)) as fh:
+            src = fh.read()
+        src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+        src = re.sub(r"//[^\n]*", " ", src)
+        h.update(" ".join(src.split()).encode())
     return h.hexdigest()[:16]
 
 

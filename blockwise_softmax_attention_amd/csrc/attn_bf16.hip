@@ -702,13 +702,16 @@ __global__ __launch_bounds__(NTHREADS, 2) void dq_bf16_kernel(KArgs a) {
 // (ds_read_b64_tr_b16): the K tile (columns = d) and the key-major dS tile
 // (columns = queries; wave w takes its 32).
 //
-// The dS stream is HBM-bound and latency-bound, so it gets the deeper ring:
-// dS of step n + DQS_SST - 1 and K of step n + 2 (K mostly hits L2) are
-// loaded while step n computes.  Every step issues the same loads in the same
-// order (past the last step the last one is fetched again into idle stages),
-// so a single vmcnt wait before the barrier finds both tiles of step n done:
-// the loads issued after K(n) are dS(n+SST-3), K(n+1) and dS(n+SST-2), and
-// dS(n) precedes K(n).
+// A step covers DQS_BN keys of one listed tile (the visited key tiles are
+// listed once per workgroup).  With 32-key steps the rings take 72.7 KB, so
+// two workgroups share a CU and one's wait, barrier and LDS latency hide
+// behind the other's MFMAs.  The dS stream gets the deeper ring: dS of step
+// n + DQS_SST - 1 and K of step n + 2 (K mostly hits L2) are loaded while
+// step n computes.  Every step issues the same loads in the same order (past
+// the last step the last one is fetched again into idle stages), so a single
+// vmcnt wait before the barrier finds both tiles of step n done: the loads
+// issued after K(n) are dS(n+SST-3), K(n+1) and dS(n+SST-2), and dS(n)
+// precedes K(n).
 #ifndef ATTN_DQS_BN
 #define ATTN_DQS_BN 32
 #endif
