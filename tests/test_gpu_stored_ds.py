@@ -143,3 +143,19 @@ def test_deterministic():
     b = run_gpu(w, inp, precise=False, stored_ds=True)
     for n in a:
         assert np.array_equal(a[n], b[n], equal_nan=True), n
+
+
+def test_full_workload_2_stored_ds():
+    """The packed-causal workload at full size (B2 H8 L2048, four segments per
+    row, per-query temperature) through the stored-dS backward, every output
+    against the oracle."""
+    from test_gpu_parity import compare_full
+    compare_full(WORKLOADS[2], precise=False)
+
+
+def test_full_workload_3_stored_ds_matches_recomputed_dq():
+    """The ALSC sliding-window workload at full size: dK, dV bit for bit and dQ
+    within rel-L2 2e-3 of the recomputing path, both in single-bf16 mode (its
+    oracle bars need hi+lo operands at this size, see test_gpu_parity)."""
+    w = WORKLOADS[3]
+    compare_paths(w, oracle=False)
