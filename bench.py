@@ -1,12 +1,20 @@
 """Benchmark: attention forward + backward TFLOP/s (unmasked FLOPs) on one MI355X.
 
 One step = one pass of the whole path over one batch of synthetic input:
-attn_fwd, attn_bwd_preprocess, attn_bwd_dq, attn_bwd_dkv.  FLOPs count only
-visible (query, key) pairs (exact count from attn_plan_count):
+attn_fwd, attn_bwd_preprocess, then the stored-dS backward (attn_bwd_dkv_ds,
+attn_bwd_dq_ds) where it applies, else attn_bwd_dq + attn_bwd_dkv.  FLOPs
+count only visible (query, key) pairs (exact count from attn_plan_count):
 forward 4 D per pair per query head, backward 10 D.
 
+The headline line is the long-context workload (B1 Hq8 L32768 D128, causal,
+ALSC cap) through the stored-dS backward.  The same run then times, after
+the headline's timed region, the recomputing backward (preprocess +
+attn_bwd_dq + attn_bwd_dkv: O(L) memory, no stored dS) on the same inputs
+("recompute_bwd") and the ranker GQA workload (B4 Hq16 Hkv4 L8192, soft-sign
+cap) in both backward modes ("ranker_gqa").
+
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 5]
-                    [--no-cpu-baseline] [--precise-ds 0|1]
+                    [--no-cpu-baseline] [--headline-only] [--precise-ds 0|1]
 
 Prints one JSON line.
 """
@@ -75,6 +83,8 @@ def parse():
                     help="1: stored-dS backward (dK/dV stores dS, dQ = dS K); 0: recomputing dQ; "
                          "-1 (default): 1 wherever it applies (bf16, single-bf16 dS)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--headline-only", action="store_true",
+                    help="time only the headline path (no recomputing-backward or ranker lines)")
     ap.add_argument("--cpu-sample-len", type=int, default=16384,
                     help="prefix length of the oracle's bounded sample")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -83,18 +93,28 @@ def parse():
     return ap.parse_args()
 
 
+def cpu_threads() -> tuple:
+    """(threads the oracle's BLAS may use, cores in this process's affinity
+    set): the affinity count, capped by OMP_NUM_THREADS where that is set."""
+    aff = len(os.sched_getaffinity(0))
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    n = min(aff, int(env)) if env.isdigit() and int(env) > 0 else aff
+    return n, aff
+
+
 def cpu_baseline(w, sample_len: int):
     """The fp64 oracle, as is, on a bounded sample of the workload: batch 0,
-    query head 0 (its KV head), the first `sample_len` positions, forward and
-    backward.  Rate = counted FLOPs of that sample / wall time."""
-    import numpy as np
-    from oracle import Params, backward, unmasked_pairs
+    query head 0 (its KV head), the first `sample_len` positions.  The forward
+    alone, then the backward (which recomputes the forward it needs); rate =
+    counted FLOPs (4 D + 10 D per visible pair) / the backward call's wall time."""
+    from oracle import Params, backward, forward, unmasked_pairs
     from workloads import make_inputs, to_f64, to_i32
+    threads, aff = cpu_threads()
     try:
-        from threadpoolctl import threadpool_info
-        threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+        from threadpoolctl import threadpool_limits
+        limiter = threadpool_limits(limits=threads)
     except Exception:  # pragma: no cover
-        threads = len(os.sched_getaffinity(0))
+        limiter = None
     ws = w.scaled(L=min(sample_len, w.L), B=1, Hq=1, Hkv=1)
     inp = make_inputs(ws)
     q, k, v, do = (to_f64(inp[n]) for n in ("q", "k", "v", "do"))
@@ -102,14 +122,109 @@ def cpu_baseline(w, sample_len: int):
     p = Params(w.sm_scale, w.causal, w.window_len, w.cap_method, w.cap, w.alpha, w.beta,
                w.z_loss_weight)
     t0 = time.perf_counter()
+    forward(q, k, v, p, temp, seg, rb)
+    t_fwd = time.perf_counter() - t0
+    t0 = time.perf_counter()
     backward(q, k, v, do, p, temp, seg, rb)
-    dt = time.perf_counter() - t0
+    t_all = time.perf_counter() - t0
+    if limiter is not None:
+        limiter.unregister()
     pairs = unmasked_pairs(ws.L, p, seg, rb, B=1)
     flops = 14.0 * w.D * pairs
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"batch 0, head 0, first {ws.L} positions of the workload, fwd+bwd in fp64 "
-                      f"({pairs} visible pairs, {dt:.1f} s)",
-            "seconds": dt}
+    return {"value": flops / t_all / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"batch 0, head 0, first {ws.L} positions of the workload in fp64 "
+                      f"({pairs} visible pairs): forward {t_fwd:.1f} s alone; backward call "
+                      f"(forward + gradients) {t_all:.1f} s",
+            "fwd_seconds": round(t_fwd, 3), "bwd_seconds": round(max(t_all - t_fwd, 0.0), 3),
+            "seconds": round(t_all, 3), "affinity_cores": aff}
+
+
+class Path:
+    """Device buffers and the launch sequence of one workload: forward,
+    preprocess, then either the stored-dS pair or the recomputing dQ + dK/dV."""
+
+    def __init__(self, w, precise: bool):
+        import torch
+        import blockwise_softmax_attention_amd as ba
+        from workloads import make_inputs
+        self.ba, self.torch, self.w = ba, torch, w
+        inp = make_inputs(w)
+        dev = {k: (v.cuda() if v is not None else None) for k, v in inp.items()}
+        self.p = ba.params_for(w, precise_ds=precise)
+        self.pairs, _ = ba.attn_plan_count(self.p, inp["segment_ids"], inp["ranker_bounds"])
+        B, L, Hq, Hkv, D = w.B, w.L, w.Hq, w.Hkv, w.D
+        f32 = dict(dtype=torch.float32, device="cuda")
+        self.o = torch.empty((B, L, Hq, D), **f32)
+        self.m = torch.empty((B, Hq, L), **f32)
+        self.l = torch.empty((B, Hq, L), **f32)
+        self.delta = torch.empty((B, Hq, L), **f32)
+        self.dq = torch.empty((B, L, Hq, D), **f32)
+        self.dk = torch.empty((B, L, Hkv, D), **f32)
+        self.dv = torch.empty((B, L, Hkv, D), **f32)
+        self.q, self.k, self.v, self.do = dev["q"], dev["k"], dev["v"], dev["do"]
+        self.temp, self.seg, self.rb = dev["temperature"], dev["segment_ids"], dev["ranker_bounds"]
+        self.ws = None
+        self.stream = torch.cuda.current_stream()
+
+    def names(self, stored: bool):
+        return (["attn_fwd", "attn_bwd_preprocess", "attn_bwd_dkv_ds", "attn_bwd_dq_ds"] if stored else
+                ["attn_fwd", "attn_bwd_preprocess", "attn_bwd_dq", "attn_bwd_dkv"])
+
+    def step(self, stored: bool, ev=None):
+        ba, p, s = self.ba, self.p, self.stream
+        if stored and self.ws is None:
+            self.ws = ba.ds_workspace(p, "cuda")
+        rec = (lambda i: ev[i].record(s)) if ev is not None else (lambda i: None)
+        rec(0)
+        ba.attn_fwd(p, self.q, self.k, self.v, self.temp, self.seg, self.rb, self.o, self.m, self.l,
+                    stream=s)
+        rec(1)
+        ba.attn_bwd_preprocess(p, self.o, self.do, self.delta, stream=s)
+        rec(2)
+        if stored:
+            ba.attn_bwd_dkv_ds(p, self.q, self.k, self.v, self.do, self.m, self.l, self.delta, self.ws,
+                               self.temp, self.seg, self.rb, self.dk, self.dv, stream=s)
+            rec(3)
+            ba.attn_bwd_dq_ds(p, self.k, self.ws, self.seg, self.rb, self.dq, stream=s)
+        else:
+            ba.attn_bwd_dq(p, self.q, self.k, self.v, self.do, self.m, self.l, self.delta, self.temp,
+                           self.seg, self.rb, self.dq, stream=s)
+            rec(3)
+            ba.attn_bwd_dkv(p, self.q, self.k, self.v, self.do, self.m, self.l, self.delta, self.temp,
+                            self.seg, self.rb, self.dk, self.dv, stream=s)
+        rec(4)
+
+    def measure(self, stored: bool, steps: int, warmup: int):
+        """Per-kernel average ms (HIP events on the launch stream) and the wall
+        time of `steps` steps bracketed by synchronisation."""
+        torch = self.torch
+        for _ in range(warmup):
+            self.step(stored)
+        torch.cuda.synchronize()
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            self.step(stored, evs[i])
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        names = self.names(stored)
+        avg = {n: sum(e[j].elapsed_time(e[j + 1]) for e in evs) / steps for j, n in enumerate(names)}
+        return avg, wall * 1e3 / steps
+
+    def summary(self, avg, peak):
+        D = self.w.D
+        fwd_flop, bwd_flop = 4.0 * D * self.pairs, 10.0 * D * self.pairs
+        names = list(avg)
+        fwd_ms = avg["attn_fwd"]
+        bwd_ms = sum(avg[n] for n in names[1:])
+        return {
+            "fwd": {"ms": round(fwd_ms, 4), "tflops": round(fwd_flop / (fwd_ms * 1e-3) / 1e12, 2),
+                    "pct_peak": round(100.0 * fwd_flop / (fwd_ms * 1e-3) / 1e12 / peak, 2)},
+            "bwd": {"ms": round(bwd_ms, 4), "tflops": round(bwd_flop / (bwd_ms * 1e-3) / 1e12, 2),
+                    "pct_peak": round(100.0 * bwd_flop / (bwd_ms * 1e-3) / 1e12 / peak, 2)},
+            "kernels_ms": {n: round(avg[n], 4) for n in names},
+        }
 
 
 def main():
@@ -121,7 +236,7 @@ def main():
 
     import torch
     import blockwise_softmax_attention_amd as ba
-    from workloads import WORKLOADS, make_inputs
+    from workloads import WORKLOADS
 
     torch.cuda.set_device(0)
     if args.copy_probe:
@@ -134,72 +249,14 @@ def main():
         return
     w = WORKLOADS[args.workload]
     precise = args.precise_ds if args.precise_ds >= 0 else (0 if args.workload in (4, 5) else 1)
-    inp = make_inputs(w)
-    dev = {k: (v.cuda() if v is not None else None) for k, v in inp.items()}
-    p = ba.params_for(w, precise_ds=bool(precise))
-    pairs, tiles = ba.attn_plan_count(p, inp["segment_ids"], inp["ranker_bounds"])
-    fwd_flop = 4.0 * w.D * pairs
-    bwd_flop = 10.0 * w.D * pairs
-
-    B, L, Hq, Hkv, D = w.B, w.L, w.Hq, w.Hkv, w.D
-    f32 = dict(dtype=torch.float32, device="cuda")
-    o = torch.empty((B, L, Hq, D), **f32)
-    m = torch.empty((B, Hq, L), **f32)
-    l = torch.empty((B, Hq, L), **f32)
-    delta = torch.empty((B, Hq, L), **f32)
-    dq = torch.empty((B, L, Hq, D), **f32)
-    dk = torch.empty((B, L, Hkv, D), **f32)
-    dv = torch.empty((B, L, Hkv, D), **f32)
-    q, k, v, do = dev["q"], dev["k"], dev["v"], dev["do"]
-    temp, seg, rb = dev["temperature"], dev["segment_ids"], dev["ranker_bounds"]
-    stream = torch.cuda.current_stream()
+    path = Path(w, bool(precise))
+    p, pairs = path.p, path.pairs
     stored = ba.stored_ds_eligible(p) if args.stored_ds < 0 else bool(args.stored_ds)
-    ws = ba.ds_workspace(p, "cuda") if stored else None
-
-    names = (["attn_fwd", "attn_bwd_preprocess", "attn_bwd_dkv_ds", "attn_bwd_dq_ds"] if stored else
-             ["attn_fwd", "attn_bwd_preprocess", "attn_bwd_dq", "attn_bwd_dkv"])
-
-    def step(ev=None):
-        if ev is not None:
-            ev[0].record(stream)
-        ba.attn_fwd(p, q, k, v, temp, seg, rb, o, m, l, stream=stream)
-        if ev is not None:
-            ev[1].record(stream)
-        ba.attn_bwd_preprocess(p, o, do, delta, stream=stream)
-        if ev is not None:
-            ev[2].record(stream)
-        if stored:
-            ba.attn_bwd_dkv_ds(p, q, k, v, do, m, l, delta, ws, temp, seg, rb, dk, dv, stream=stream)
-            if ev is not None:
-                ev[3].record(stream)
-            ba.attn_bwd_dq_ds(p, k, ws, seg, rb, dq, stream=stream)
-        else:
-            ba.attn_bwd_dq(p, q, k, v, do, m, l, delta, temp, seg, rb, dq, stream=stream)
-            if ev is not None:
-                ev[3].record(stream)
-            ba.attn_bwd_dkv(p, q, k, v, do, m, l, delta, temp, seg, rb, dk, dv, stream=stream)
-        if ev is not None:
-            ev[4].record(stream)
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(evs[i])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-
-    per = {n: [] for n in names}
-    for e in evs:
-        for j, n in enumerate(names):
-            per[n].append(e[j].elapsed_time(e[j + 1]))
-    avg = {n: sum(x) / len(x) for n, x in per.items()}
-    step_ms = wall * 1e3 / args.steps
-    fwd_ms = avg["attn_fwd"]
-    bwd_ms = sum(avg[n] for n in names[1:])
+    names = path.names(stored)
+    B, L, Hq, Hkv, D = w.B, w.L, w.Hq, w.Hkv, w.D
+    fwd_flop = 4.0 * D * pairs
+    bwd_flop = 10.0 * D * pairs
+    avg, step_ms = path.measure(stored, args.steps, args.warmup)
     value = (fwd_flop + bwd_flop) / (step_ms * 1e-3) / 1e12
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
 
@@ -231,17 +288,45 @@ def main():
                    "head_dim": D, "cap": w.cap_method, "causal": w.causal, "window": w.window_len,
                    "precise_ds": bool(precise), "stored_ds": stored, "visible_pairs": pairs},
         "pct_peak": round(100.0 * value / peak, 2),
-        "fwd": {"ms": round(fwd_ms, 4), "tflops": round(fwd_flop / (fwd_ms * 1e-3) / 1e12, 2),
-                "pct_peak": round(100.0 * fwd_flop / (fwd_ms * 1e-3) / 1e12 / peak, 2)},
-        "bwd": {"ms": round(bwd_ms, 4), "tflops": round(bwd_flop / (bwd_ms * 1e-3) / 1e12, 2),
-                "pct_peak": round(100.0 * bwd_flop / (bwd_ms * 1e-3) / 1e12 / peak, 2)},
-        "kernels_ms": {n: round(avg[n], 4) for n in names},
-        "preprocess_gbps": round(pre_bytes / (avg["attn_bwd_preprocess"] * 1e-3) / 1e9, 1),
-        # stored-dS dQ: workspace bytes (every band tile; tiles skipped by a mask
-        # are not read, so this bounds the dS bytes streamed) per launch time
-        "dq_ds_gbps": (round(ws.numel() / (avg["attn_bwd_dq_ds"] * 1e-3) / 1e9, 1) if stored else None),
-        "roofline": roofline,
     }
+    out.update(path.summary(avg, peak))
+    out["preprocess_gbps"] = round(pre_bytes / (avg["attn_bwd_preprocess"] * 1e-3) / 1e9, 1)
+    # stored-dS dQ: workspace bytes (every band tile; tiles skipped by a mask
+    # are not read, so this bounds the dS bytes streamed) per launch time
+    out["dq_ds_gbps"] = (round(path.ws.numel() / (avg["attn_bwd_dq_ds"] * 1e-3) / 1e9, 1)
+                         if stored else None)
+    out["roofline"] = roofline
+
+    if not args.headline_only:
+        # The O(L)-memory backward of the pages (preprocess + recomputing dQ +
+        # dK/dV, no stored dS) on the same inputs, timed after the headline.
+        if stored:
+            ravg, _ = path.measure(False, args.steps, args.warmup)
+            r = path.summary(ravg, peak)
+            out["recompute_bwd"] = {"workload": w.name, "precise_ds": bool(precise), **r["bwd"],
+                                    "kernels_ms": {k: v for k, v in r["kernels_ms"].items()
+                                                   if k != "attn_fwd"}}
+        if args.workload == 5:
+            # the second workload at L >= 8192: ranker mask, GQA, soft-sign cap
+            path.ws = None
+            del path
+            torch.cuda.empty_cache()
+            w4 = WORKLOADS[4]
+            p4 = Path(w4, False)
+            st4 = ba.stored_ds_eligible(p4.p)
+            a4, s4 = p4.measure(st4, args.steps, args.warmup)
+            r4 = p4.summary(a4, peak)
+            ra4, _ = p4.measure(False, args.steps, args.warmup)
+            rr4 = p4.summary(ra4, peak)
+            out["ranker_gqa"] = {
+                "workload": w4.name, "batch": w4.B, "seq_len": w4.L, "q_heads": w4.Hq,
+                "kv_heads": w4.Hkv, "visible_pairs": p4.pairs, "precise_ds": False,
+                "stored_ds": st4, "ms_per_step": round(s4, 4),
+                "tflops": round(14.0 * w4.D * p4.pairs / (s4 * 1e-3) / 1e12, 2),
+                "fwd": r4["fwd"], "bwd": r4["bwd"], "kernels_ms": r4["kernels_ms"],
+                "recompute_bwd": {**rr4["bwd"], "kernels_ms": {k: v for k, v in rr4["kernels_ms"].items()
+                                                               if k != "attn_fwd"}},
+            }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_sample_len)
     print(json.dumps(out), flush=True)

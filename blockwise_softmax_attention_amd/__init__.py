@@ -275,6 +275,22 @@ def stored_ds_eligible(p: AttnParams, dtemp: bool = False) -> bool:
     return p.dtype == ATTN_BF16 and not p.precise_ds and not dtemp
 
 
+# Largest stored-dS workspace attention_forward_backward allocates on its own
+# (16 GiB, about 6% of one GPU's 288 GB).  The workspace grows with the number
+# of visited 128 x 128 blocks, i.e. with L^2 (8.6 GB for 8 causal heads at
+# L = 32768, ~137 GB at L = 131072); beyond this cap the recomputing dQ
+# (O(L) memory, as the pages' backward) is taken unless the caller asks for
+# the stored-dS path or hands in a workspace.
+STORED_DS_AUTO_MAX_BYTES = 16 << 30
+
+
+def stored_ds_auto(p: AttnParams, dtemp: bool = False,
+                   max_bytes: int = STORED_DS_AUTO_MAX_BYTES) -> bool:
+    """Whether attention_forward_backward takes the stored-dS backward when the
+    caller leaves the choice to it: eligible, and its workspace fits max_bytes."""
+    return stored_ds_eligible(p, dtemp) and attn_bwd_ds_workspace_size(p) <= max_bytes
+
+
 def attn_plan_count(p: AttnParams, segment_ids=None, ranker_bounds=None):
     """(unmasked pairs, visited forward tiles), both summed over batch and heads.
     Host-side; segment_ids / ranker_bounds are CPU int32 tensors or None."""
@@ -302,13 +318,14 @@ def attention_forward_backward(p: AttnParams, q, k, v, d_o, temperature=None, se
     """One pass of the whole path: forward, then preprocess, dQ and dK/dV
     (and, with dtemp=True, the temperature gradient (B, L)).  stored_ds: use
     the stored-dS backward (dK/dV, then dQ from the stored dS); None picks it
-    whenever it applies (stored_ds_eligible).  ds: a workspace to reuse
-    (uint8, at least attn_bwd_ds_workspace_size bytes); one is allocated if
-    not given."""
+    when it applies and either a workspace ds is given or the one it would
+    allocate fits STORED_DS_AUTO_MAX_BYTES (stored_ds_auto), else the
+    recomputing dQ.  ds: a workspace to reuse (uint8, at least
+    attn_bwd_ds_workspace_size bytes); one is allocated if not given."""
+    if stored_ds is None:
+        stored_ds = stored_ds_eligible(p, dtemp) if ds is not None else stored_ds_auto(p, dtemp)
     o, m, l = attn_fwd(p, q, k, v, temperature, segment_ids, ranker_bounds, stream=stream)
     delta = attn_bwd_preprocess(p, o, d_o, stream=stream)
-    if stored_ds is None:
-        stored_ds = stored_ds_eligible(p, dtemp)
     if stored_ds:
         if dtemp:
             raise ValueError("the temperature gradient needs the recomputing dQ (stored_ds=False)")

@@ -284,7 +284,7 @@ def backward(q, k, v, do, p: Params, temperature=None, segment_ids=None, ranker_
                              heads=range(g * G, (g + 1) * G), batches=[b], row_chunk=row_chunk)
         hs = slice(g * G, (g + 1) * G)
         o[b, :, hs], m[b, hs], l[b, hs] = o_[b, :, hs], m_[b, hs], l_[b, hs]
-    delta = np.einsum("blhd,blhd->bhl", o, do)
+    delta = preprocess(o, do)
     dq = np.full((B, L, Hq, D), np.nan)
     dk = np.full((B, L, Hkv, D), np.nan)
     dv = np.full((B, L, Hkv, D), np.nan)

@@ -259,3 +259,28 @@ def test_ds_calls_reject_null_workspace_before_launch():
     st = lib.attn_bwd_dkv_ds(ctypes.byref(cp), a16, a16, a16, None, None, None, a16, a16, a16, a16,
                              a16, a16, a16, need - 1, None)
     assert st == -2 and b"needed" in lib.attn_last_error()
+
+
+def test_stored_ds_auto_selection_cap():
+    """attention_forward_backward takes the stored-dS backward on its own only
+    when it applies and its workspace fits STORED_DS_AUTO_MAX_BYTES."""
+    cap = ba.STORED_DS_AUTO_MAX_BYTES
+    assert cap == 16 << 30
+    long_ctx = base_params(batch=1, seq_len=32768, q_heads=8, kv_heads=8, head_dim=128,
+                           causal=True, precise_ds=False)
+    need = ba.attn_bwd_ds_workspace_size(long_ctx)
+    assert need == 8 * (256 * 257 // 2) * 32768 and need <= cap
+    assert ba.stored_ds_auto(long_ctx)
+    # four times the length: ~16x the workspace, past the cap -> recomputing dQ
+    longer = base_params(batch=1, seq_len=131072, q_heads=8, kv_heads=8, head_dim=128,
+                         causal=True, precise_ds=False)
+    assert ba.attn_bwd_ds_workspace_size(longer) > cap
+    assert not ba.stored_ds_auto(longer)
+    # a caller's own cap
+    assert not ba.stored_ds_auto(long_ctx, max_bytes=need - 1)
+    assert ba.stored_ds_auto(long_ctx, max_bytes=need)
+    # not eligible: hi+lo operands, float inputs, temperature gradient
+    assert not ba.stored_ds_auto(base_params(precise_ds=True))
+    assert not ba.stored_ds_auto(base_params(dtype=ba.ATTN_F32, precise_ds=False))
+    assert not ba.stored_ds_auto(base_params(precise_ds=False), dtemp=True)
+    assert ba.stored_ds_auto(base_params(precise_ds=False))

@@ -432,6 +432,33 @@ def test_delta_identity_and_row_helpers():
     assert np.allclose(kv["dv"], full["dv"][0, keys, 1], atol=1e-13)
 
 
+def test_preprocess_delta_identity_and_axis_order():
+    """preprocess (delta = sum_d O dO, laid out (B, Hq, L)) against the identity
+    delta_i = sum_j P_ij dP_ij with dP = dO V^T, where P and O come from torch's
+    softmax on CPU, not from the oracle.  B, L, Hq and D all differ, so a
+    reduction over the wrong axis or a transposed output fails."""
+    rng = np.random.default_rng(12)
+    B, L, Hq, Hkv, D = 2, 7, 3, 1, 5
+    q, do = rnd(rng, B, L, Hq, D), rnd(rng, B, L, Hq, D)
+    k, v = rnd(rng, B, L, Hkv, D), rnd(rng, B, L, Hkv, D)
+    o = np.zeros((B, L, Hq, D))
+    ref = np.zeros((B, Hq, L))
+    for b in range(B):
+        for hq in range(Hq):
+            s = torch.from_numpy(0.3 * q[b, :, hq] @ k[b, :, 0].T)
+            P = torch.softmax(s, dim=-1).numpy()
+            o[b, :, hq] = P @ v[b, :, 0]
+            dP = do[b, :, hq] @ v[b, :, 0].T
+            ref[b, hq] = (P * dP).sum(axis=1)
+    from oracle import preprocess
+    got = preprocess(o, do)
+    assert got.shape == (B, Hq, L)
+    assert np.allclose(got, ref, rtol=0, atol=1e-12)
+    # the planted mistake of an output in (B, L, Hq) order read as (B, Hq, L)
+    wrong = np.einsum("blhd,blhd->blh", o, do).reshape(B, Hq, L)
+    assert not np.allclose(wrong, ref, atol=1e-6)
+
+
 def test_cap_golden_closed_forms():
     import json
     import os
