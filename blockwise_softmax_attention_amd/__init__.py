@@ -7,7 +7,8 @@ missing or the tensors are not on the GPU, the calls raise.
 
 Names mirror the C ABI: attn_fwd, attn_bwd_preprocess, attn_bwd_dq,
 attn_bwd_dkv, attn_bwd_ds_workspace_size, attn_bwd_dkv_ds, attn_bwd_dq_ds,
-attn_reduce_heads, attn_ranker_bounds, attn_plan_count, attn_check_params.
+attn_bwd_ds_static, attn_reduce_heads, attn_ranker_bounds, attn_plan_count,
+attn_check_params.
 """
 from __future__ import annotations
 
@@ -86,7 +87,12 @@ _FN_SIGS = {
     "attn_bwd_dkv_ds": [ctypes.POINTER(_CParams), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                         ctypes.c_uint64, _P],
     "attn_bwd_dq_ds": [ctypes.POINTER(_CParams), _P, _P, _P, _P, ctypes.c_uint64, _P, _P],
+    "attn_bwd_ds_static": [ctypes.POINTER(_CParams), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                           _P, _P],
 }
+
+# Size of the library's fixed stored-dS array (include/attn.h, ATTN_STATIC_DS_BYTES).
+ATTN_STATIC_DS_BYTES = 128 << 20
 
 
 def load_library(path: str = LIB_PATH):
@@ -267,6 +273,28 @@ def attn_bwd_dq_ds(p: AttnParams, k, ds, segment_ids=None, ranker_bounds=None, d
         _ptr(ranker_bounds, "ranker_bounds", torch.int32), _ptr(ds, "ds", torch.uint8),
         int(ds.numel()), _ptr(dq, "dq", torch.float32), _stream(stream)))
     return dq
+
+
+def attn_bwd_ds_static(p: AttnParams, q, k, v, d_o, m, l, delta, temperature=None, segment_ids=None,
+                       ranker_bounds=None, dq=None, dk=None, dv=None, stream=None):
+    """The stored-dS backward with the library's fixed dS array as its
+    workspace (the C entry point allocates nothing; outputs not given are
+    allocated here by torch).  Returns (dq, dk, dv)."""
+    dq = torch.empty((p.batch, p.seq_len, p.q_heads, p.head_dim), dtype=torch.float32,
+                     device=q.device) if dq is None else dq
+    shape = (p.batch, p.seq_len, p.kv_heads, p.head_dim)
+    dk = torch.empty(shape, dtype=torch.float32, device=q.device) if dk is None else dk
+    dv = torch.empty(shape, dtype=torch.float32, device=q.device) if dv is None else dv
+    dt = _in_dtype(p)
+    cp = p.to_c()
+    _check(load_library().attn_bwd_ds_static(
+        ctypes.byref(cp), _ptr(q, "q", dt), _ptr(k, "k", dt), _ptr(v, "v", dt),
+        _ptr(temperature, "temperature", torch.float32), _ptr(segment_ids, "segment_ids", torch.int32),
+        _ptr(ranker_bounds, "ranker_bounds", torch.int32), _ptr(d_o, "d_o", dt),
+        _ptr(m, "m", torch.float32), _ptr(l, "l", torch.float32), _ptr(delta, "delta", torch.float32),
+        _ptr(dq, "dq", torch.float32), _ptr(dk, "dk", torch.float32), _ptr(dv, "dv", torch.float32),
+        _stream(stream)))
+    return dq, dk, dv
 
 
 def stored_ds_eligible(p: AttnParams, dtemp: bool = False) -> bool:

@@ -4,6 +4,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 #include <string>
 #include <unordered_map>
 #include <vector>
@@ -167,6 +168,40 @@ attn_status hip_status(hipError_t e, const char* what) {
   return ATTN_OK;
 }
 
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// Allocation-free stored-dS backward: the dS workspace is this fixed device
+// array.  Host code never passes `scratch` itself to a kernel (on the host
+// it names a stand-in, not device memory): the device address comes from
+// hipGetSymbolAddress, once per device, and only that address is used.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[ATTN_STATIC_DS_BYTES];
+
+namespace {
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[MAX_DEVICES] = {};
+
+// Device address of `scratch` on the current device (looked up on the first
+// call with that device current, then kept).
+attn_status scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(ATTN_ERR_HIP, std::string("hipGetDevice: ") + hipGetErrorString(e));
+  if (dev < 0 || dev >= MAX_DEVICES)
+    return fail(ATTN_ERR_HIP, "device index " + std::to_string(dev) + " out of range");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch[dev] == nullptr) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || ptr == nullptr)
+      return fail(ATTN_ERR_HIP, std::string("hipGetSymbolAddress(scratch): ") + hipGetErrorString(e));
+    g_scratch[dev] = ptr;
+  }
+  *out = g_scratch[dev];
+  return ATTN_OK;
+}
 }  // namespace
 
 extern "C" {
@@ -368,6 +403,51 @@ attn_status attn_bwd_dq_ds(const attn_params* p, const void* k, const int32_t* s
   a.n_items = a.B * a.Hq * a.n_q_tiles;
   return hip_status(attn::launch_dq_ds_bf16(a, p->head_dim, (hipStream_t)stream),
                     "attn_bwd_dq_ds launch");
+}
+
+attn_status attn_bwd_ds_static(const attn_params* p, const void* q, const void* k, const void* v,
+                               const float* temperature, const int32_t* segment_ids,
+                               const int32_t* ranker_bounds, const void* d_o, const float* m,
+                               const float* l, const float* delta, float* dq, float* dk, float* dv,
+                               void* stream) {
+  ATTN_TRY(check_ds_params(p));
+  ATTN_TRY(check_bwd_inputs(p, q, k, v, temperature, segment_ids, ranker_bounds, d_o, m, l, delta));
+  ATTN_TRY(check_ptr(dq, "dq", 16));
+  ATTN_TRY(check_ptr(dk, "dk", 16));
+  ATTN_TRY(check_ptr(dv, "dv", 16));
+  uint64_t need = 0;
+  ATTN_TRY(attn_bwd_ds_workspace_size(p, &need));
+  if (need > ATTN_STATIC_DS_BYTES)
+    return fail(ATTN_ERR_SHAPE, "the stored-dS workspace of this shape (" + std::to_string(need) +
+                                    " bytes) exceeds the library's fixed array (" +
+                                    std::to_string((unsigned long long)ATTN_STATIC_DS_BYTES) +
+                                    " bytes): use attn_bwd_dkv_ds / attn_bwd_dq_ds with a caller "
+                                    "workspace");
+  void* ws = nullptr;
+  ATTN_TRY(scratch_address(&ws));
+  attn::KArgs a = make_args(p, temperature, segment_ids, ranker_bounds);
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.dout = d_o;
+  a.m_in = m;
+  a.l_in = l;
+  a.delta_in = delta;
+  a.out0 = dk;
+  a.out1 = dv;
+  a.ds = ws;
+  a.ds_slots = ds_slots(p);
+  a.n_items = a.B * a.Hkv * a.n_kv_tiles;
+  ATTN_TRY(hip_status(attn::launch_dkv_ds_bf16(a, p->head_dim, effective_cap(p), (hipStream_t)stream),
+                      "attn_bwd_ds_static dK/dV launch"));
+  attn::KArgs b = make_args(p, nullptr, segment_ids, ranker_bounds);
+  b.k = k;
+  b.ds = ws;
+  b.ds_slots = ds_slots(p);
+  b.out0 = dq;
+  b.n_items = b.B * b.Hq * b.n_q_tiles;
+  return hip_status(attn::launch_dq_ds_bf16(b, p->head_dim, (hipStream_t)stream),
+                    "attn_bwd_ds_static dQ launch");
 }
 
 attn_status attn_plan_count(const attn_params* p, const int32_t* seg, const int32_t* bounds,

@@ -37,7 +37,9 @@
  *   dV are always float.
  *
  * Ownership: the caller allocates and owns every buffer; the library keeps
- * no state between calls and allocates no device memory.  Every compute call
+ * no state between calls and allocates no device memory (the one exception,
+ * attn_bwd_ds_static, uses a fixed device array of the library instead of a
+ * caller's workspace).  Every compute call
  * only enqueues kernels on `stream` (a hipStream_t; NULL = default stream) and
  * returns; the caller synchronises.  Outputs are overwritten, never
  * accumulated, and no call uses atomics: results are bitwise reproducible.
@@ -103,8 +105,13 @@ typedef struct {
 /* With segment ids the workgroup-local segment-skip table bounds L further. */
 #define ATTN_MAX_SEQ_LEN_SEGMENTS 131072
 
-/* Forward.  temperature NULL means 1 everywhere; segment_ids NULL means one
- * segment; ranker_bounds NULL means no ranker mask.  Writes o, m, l. */
+/* Forward (triton_kernels.py page, make_triton_forward_kernel: scores, cap and
+ * temperature inside the online-softmax update, the (l, m) residuals; caps from
+ * the mosaic_backward.py page, _apply_cap_mosaic; ranker mask from its
+ * ranker_mask_mosaic_kv_q).  temperature NULL means 1 everywhere; segment_ids
+ * NULL means one segment; ranker_bounds NULL means no ranker mask.  Writes o
+ * (B, L, Hq, D) float and m, l (B, Hq, L) float, m in natural-log units; a
+ * row that sees no key gets o = 0, m = -inf, l = 0. */
 attn_status attn_fwd(const attn_params* params, const void* q, const void* k, const void* v,
                      const float* temperature, const int32_t* segment_ids,
                      const int32_t* ranker_bounds, float* o, float* m, float* l,
@@ -196,6 +203,33 @@ attn_status attn_bwd_dkv_ds(const attn_params* params, const void* q, const void
 attn_status attn_bwd_dq_ds(const attn_params* params, const void* k, const int32_t* segment_ids,
                            const int32_t* ranker_bounds, const void* ds, uint64_t ds_bytes,
                            float* dq, void* stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * stored-dS backward, attn_bwd_dkv_ds then attn_bwd_dq_ds on `stream`, with
+ * the dS workspace taken from a fixed device array of the library instead of
+ * a caller's buffer.  Same inputs as attn_bwd_dkv_ds (and the same
+ * requirements: bf16, precise_ds == 0); writes dq (B, L, Hq, D), dk and dv
+ * (B, L, Hkv, D) float, bit for bit what that pair of calls writes.
+ *
+ * Limit: attn_bwd_ds_workspace_size(params) must not exceed
+ * ATTN_STATIC_DS_BYTES (128 MiB), else ATTN_ERR_SHAPE and nothing is
+ * launched (the packed-causal B2 Hq8 L2048 and window B1 Hq16 L4096 W512
+ * shapes need 68 and 75 MiB; the long-context and ranker shapes do not fit).
+ * The array is reserved on each GPU the library runs on and held until the
+ * process ends; its address is looked up once per device, on the first call
+ * with that device current.  This call makes no hipMalloc, hipFree or other
+ * allocating call.  Every call on one GPU shares that GPU's array, which keeps
+ * the last call's contents (no part of it needs to start at zero: the dK/dV
+ * kernel writes every tile the dQ kernel then reads), so calls that overlap
+ * on one GPU (two streams or two host threads) race: the caller serialises
+ * them. */
+#define ATTN_STATIC_DS_BYTES (128ull << 20)
+attn_status attn_bwd_ds_static(const attn_params* params, const void* q, const void* k,
+                               const void* v, const float* temperature, const int32_t* segment_ids,
+                               const int32_t* ranker_bounds, const void* d_o, const float* m,
+                               const float* l, const float* delta, float* dq, float* dk, float* dv,
+                               void* stream);
 
 /* Host only, no GPU needed: exact number of visible (query, key) pairs summed
  * over batch rows and query heads, and the number of (query tile, key tile)

@@ -284,3 +284,35 @@ def test_stored_ds_auto_selection_cap():
     assert not ba.stored_ds_auto(base_params(dtype=ba.ATTN_F32, precise_ds=False))
     assert not ba.stored_ds_auto(base_params(precise_ds=False), dtemp=True)
     assert ba.stored_ds_auto(base_params(precise_ds=False))
+
+
+def test_static_ds_entry_point_rejects_shapes_beyond_its_array_before_launch():
+    """attn_bwd_ds_static refuses a shape whose stored-dS workspace exceeds the
+    library's fixed array, on the host, before touching the GPU."""
+    lib = ba.load_library()
+    good = 4096
+    big = base_params(batch=1, seq_len=32768, q_heads=8, kv_heads=8, head_dim=128, causal=True,
+                      precise_ds=False)
+    assert ba.attn_bwd_ds_workspace_size(big) > ba.ATTN_STATIC_DS_BYTES
+    cp = big.to_c()
+    # q, k, v, temp, seg, bounds, d_o, m, l, delta, dq, dk, dv, stream
+    st = lib.attn_bwd_ds_static(ctypes.byref(cp), good, good, good, None, None, None, good, good, good,
+                                good, good, good, good, None)
+    assert st == -2
+    assert "fixed array" in lib.attn_last_error().decode()
+    # the requirements of the stored-dS backward hold here too
+    cp = base_params(precise_ds=True).to_c()
+    assert lib.attn_bwd_ds_static(ctypes.byref(cp), good, good, good, None, None, None, good, good,
+                                  good, good, good, good, good, None) == -4
+    cp = base_params(precise_ds=False).to_c()
+    assert lib.attn_bwd_ds_static(ctypes.byref(cp), good, good, good, None, None, None, good, good,
+                                  good, good, None, good, good, None) == -1
+    assert "dq" in lib.attn_last_error().decode()
+    # the two sizes the header quotes as fitting
+    packed = base_params(batch=2, seq_len=2048, q_heads=8, kv_heads=8, head_dim=128, causal=True,
+                         precise_ds=False)
+    window = base_params(batch=1, seq_len=4096, q_heads=16, kv_heads=16, head_dim=128, causal=True,
+                         window_len=512, precise_ds=False)
+    for p, mib in ((packed, 68), (window, 75)):
+        n = ba.attn_bwd_ds_workspace_size(p)
+        assert n <= ba.ATTN_STATIC_DS_BYTES and abs(n / 2**20 - mib) < 1, (n, mib)
