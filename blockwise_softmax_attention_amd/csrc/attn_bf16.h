@@ -4,14 +4,21 @@
 // Tile layout.  A tile of ROWS rows x D bf16 columns occupies ROWS * 2D bytes
 // of LDS with no padding.  LDS row lr holds the tile's row pi(lr) (bits 2 and 3
 // swapped inside each 32-row block, see attn_device.h), and its 16-byte chunk c
-// sits at position c ^ swz(lr).  With
-//   swz(lr) = 2 (lr & 3) + ((lr >> 2) & 1) + 8 ((lr >> 3) & 1)   (mod D / 8)
-// both access patterns hit distinct banks:
-//   * row fragments (A operand, reduction over D): 8 consecutive LDS rows,
-//     one chunk each -> 8 distinct positions;
+// sits at position c ^ swz(lr), where the bits of swz(lr) (mod D / 8) are
+//   bit 0 = lr2,  bit 1 = lr0,  bit 2 = lr1,  bit 3 = lr0 ^ lr3.
+// With 256-byte rows (D = 128) both access patterns then hit distinct banks,
+// whether the LDS serves 128 or 256 bytes per clock (32 or 64 banks):
+//   * row fragments (A operand, reduction over D): 16 consecutive LDS rows,
+//     one chunk each -> 16 distinct chunk positions (bits 0-3 of swz are a
+//     bijection of lr bits 0-3);
 //   * transposed fragments (ds_read_b64_tr_b16, reduction over the tile rows):
-//     16 lanes read 4 consecutive rows x 2 adjacent chunks -> 8 distinct
-//     positions.
+//     32 lanes read 4 consecutive rows x 4 adjacent chunks (an aligned group,
+//     differing in chunk bits 0-1) -> 16 distinct positions, because as lr
+//     bits 0-1 run over the 4 rows, swz bits 2-3 (and, for 16 lanes, bits 1-2)
+//     take 4 distinct values.
+// (The previous form 2 (lr & 3) + ((lr >> 2) & 1) + 8 ((lr >> 3) & 1) left
+// the transposed reads two-way conflicted on 64 banks: only swz bit 2 varied
+// with lr bits 0-1.)
 //
 // Loads.  global_load_lds_dwordx4 writes lane l's 16 bytes to LDS address
 // M0 + 16 l, so each instruction fills 1 KB of LDS; the lane -> (row, chunk)
@@ -89,7 +96,8 @@ struct BTile {
   static_assert(NINST % NW == 0, "tile must split evenly over the waves");
 
   __device__ __forceinline__ static int swz(int lr) {
-    return (2 * (lr & 3) + ((lr >> 2) & 1) + 8 * ((lr >> 3) & 1)) & (CPR - 1);
+    return (((lr >> 2) & 1) | ((lr & 1) << 1) | (((lr >> 1) & 1) << 2) | (((lr ^ (lr >> 3)) & 1) << 3)) &
+           (CPR - 1);
   }
 
   // Per-lane part of every load address, computed once: load n = wave + NW i
