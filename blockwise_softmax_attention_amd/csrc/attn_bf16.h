@@ -55,6 +55,12 @@ __device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t
   asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(m0)
                : "memory", "m0");
 }
+// The same load marked non-temporal (nt): for data read once, so that it does
+// not evict lines that other workgroups of the XCD read again from L2.
+__device__ __forceinline__ void dma16_nt(const void* sbase, uint32_t voff, uint32_t m0) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1 nt" ::"v"(voff), "s"(sbase), "s"(m0)
+               : "memory", "m0");
+}
 
 // A pointer the caller knows to be the same on every lane, moved to scalar
 // registers.
@@ -126,12 +132,18 @@ struct BTile {
   // element (0, 0) of the tile (wave-uniform); rows >= rows_valid read row
   // rows_valid - 1 (finite data the masks zero; only the last tile of a
   // sequence has such rows).
+  template <bool NT = false>
   __device__ __forceinline__ static void issue_one(uint32_t lds_base, const bf16* gbase, uint32_t rsb,
                                                    int rows_valid, const Lane& ln, int wave, int i) {
     const int n = wave + NW * i;
     const uint32_t lim = (uint32_t)(rows_valid - 1) * rsb + ln.cbyte;
     const uint32_t off = imin_u(ln.off0 + (uint32_t)(i * RPI * NW) * rsb, lim);
-    dma16(uniform_ptr(gbase), off, (uint32_t)__builtin_amdgcn_readfirstlane(lds_base + n * 1024));
+    const uint32_t m0 = (uint32_t)__builtin_amdgcn_readfirstlane(lds_base + n * 1024);
+    if (NT) {
+      dma16_nt(uniform_ptr(gbase), off, m0);
+    } else {
+      dma16(uniform_ptr(gbase), off, m0);
+    }
   }
 
   // All of this wave's loads of one tile.

@@ -711,7 +711,10 @@ __global__ __launch_bounds__(NTHREADS, 2) void dq_bf16_kernel(KArgs a) {
 // the last step the last one is fetched again into idle stages), so a single
 // vmcnt wait before the barrier finds both tiles of step n done: the loads
 // issued after K(n) are dS(n+SST-3), K(n+1) and dS(n+SST-2), and dS(n)
-// precedes K(n).
+// precedes K(n).  The dS tiles, read once, are loaded non-temporal (nt) so
+// that their stream does not push out of L2 the K tiles the XCD's other
+// workgroups read again (HBM bytes per launch on the long-context workload
+// 9.39 -> 8.83 GB fetched, 2% faster).
 #ifndef ATTN_DQS_BN
 #define ATTN_DQS_BN 32
 #endif
@@ -800,7 +803,8 @@ __global__ __launch_bounds__(NTHREADS, DQS_WG_PER_CU) void dq_ds_bf16_kernel(KAr
   auto issue_s = [&](int n, int stg) {
     const bf16* g = Sb + ((long)sList[n >> PSH] * DS_ELEMS + (long)(n & (PARTS - 1)) * BN * DS_T);
 #pragma unroll
-    for (int i = 0; i < NS; ++i) ST::issue_one(lds_offset(sS[stg]), g, S_RSB, BN, sln, wave, i);
+    for (int i = 0; i < NS; ++i)   // read once: non-temporal, K stays in L2
+      ST::template issue_one<true>(lds_offset(sS[stg]), g, S_RSB, BN, sln, wave, i);
   };
 
   f32x16 dqacc[NDB];
