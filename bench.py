@@ -44,14 +44,14 @@ HBM_GBPS = 8000.0
 KERNEL_SOURCES = ["attn_bf16.hip", "attn_bf16.h", "attn_device.h", "attn_tiles.h",
                   "attn_internal.h", "attn_bwd_common.h", "attn_preprocess.hip"]
 MEASURED_TRAFFIC = {
-    ("ee938ed215a19beb", 5, 0): {"attn_fwd": (239660 * 2.0 + 133984) * 1024,
+    ("18a2bebc18df7f69", 5, 0): {"attn_fwd": (231891 * 2.0 + 133950) * 1024,
                                  "attn_bwd_preprocess": (98333 * 2.0 + 4097) * 1024,
-                                 "attn_bwd_dkv_ds": (619389 * 2.0 + 8713805) * 1024,
-                                 "attn_bwd_dq_ds": (4696666 * 2.0 + 131120) * 1024},
-    ("ee938ed215a19beb", 4, 0): {"attn_fwd": (548384 * 2.0 + 266295) * 1024,
-                                 "attn_bwd_preprocess": (196638 * 2.0 + 16409) * 1024,
-                                 "attn_bwd_dkv_ds": (1051513 * 2.0 + 6423406) * 1024,
-                                 "attn_bwd_dq_ds": (3728650 * 2.0 + 262167) * 1024},
+                                 "attn_bwd_dkv_ds": (603207 * 2.0 + 8709541) * 1024,
+                                 "attn_bwd_dq_ds": (4310823 * 2.0 + 131081) * 1024},
+    ("18a2bebc18df7f69", 4, 0): {"attn_fwd": (465756 * 2.0 + 266241) * 1024,
+                                 "attn_bwd_preprocess": (196637 * 2.0 + 16403) * 1024,
+                                 "attn_bwd_dkv_ds": (1037800 * 2.0 + 6423378) * 1024,
+                                 "attn_bwd_dq_ds": (3557066 * 2.0 + 262153) * 1024},
 }
 
 
@@ -318,12 +318,22 @@ def main():
             r4 = p4.summary(a4, peak)
             ra4, _ = p4.measure(False, args.steps, args.warmup)
             rr4 = p4.summary(ra4, peak)
+            alg4 = {"attn_fwd": 4.0 * w4.D * p4.pairs, "attn_bwd_dkv_ds": 8.0 * w4.D * p4.pairs,
+                    "attn_bwd_dq_ds": 2.0 * w4.D * p4.pairs, "attn_bwd_dkv": 8.0 * w4.D * p4.pairs,
+                    "attn_bwd_dq": 6.0 * w4.D * p4.pairs}
+            dom4 = max((n for n in a4 if n in alg4), key=lambda n: a4[n])
+            ach4 = alg4[dom4] / (a4[dom4] * 1e-3) / 1e12
+            meas4 = MEASURED_TRAFFIC.get((kernel_source_hash(), 4, 0))
             out["ranker_gqa"] = {
                 "workload": w4.name, "batch": w4.B, "seq_len": w4.L, "q_heads": w4.Hq,
                 "kv_heads": w4.Hkv, "visible_pairs": p4.pairs, "precise_ds": False,
                 "stored_ds": st4, "ms_per_step": round(s4, 4),
                 "tflops": round(14.0 * w4.D * p4.pairs / (s4 * 1e-3) / 1e12, 2),
                 "fwd": r4["fwd"], "bwd": r4["bwd"], "kernels_ms": r4["kernels_ms"],
+                "roofline": {"bound": "mfma", "kernel": dom4, "achieved": round(ach4, 2), "peak": peak,
+                             "unit": "TFLOP/s", "frac": round(ach4 / peak, 4),
+                             "traffic": None if meas4 is None else int(meas4[dom4]),
+                             "traffic_unit": "bytes per launch (HBM, calibrated)"},
                 "recompute_bwd": {**rr4["bwd"], "kernels_ms": {k: v for k, v in rr4["kernels_ms"].items()
                                                                if k != "attn_fwd"}},
             }

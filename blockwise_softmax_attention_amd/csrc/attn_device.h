@@ -132,7 +132,7 @@ __device__ __forceinline__ int xcd_remap(int bid, int n) {
 // temp cap'(sm_scale x) sm_scale = R g(aux).  The bfloat16 path uses the
 // hardware exp2 / reciprocal (errors near 1 ulp, far below bf16 operand
 // rounding); the float path uses libm formulations that avoid cancellation
-// near zero.  Host-side constants per cap (attn_api.cpp):
+// near zero.  Host-side constants per cap (attn_api.hip, make_args):
 //   none            f = x                 kmul = sm log2e            kadd = 0
 //   tanh, fast      f = 1/(1+e^{2y})      kmul = -2 cap log2e        kadd = cap log2e
 //   tanh, float     f = tanh(y)           kmul = cap log2e           kadd = 0
