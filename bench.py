@@ -90,6 +90,9 @@ def parse():
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (HBM counter "
                          "calibration) and exit")
+    ap.add_argument("--gemm-probe", type=int, default=0, metavar="N",
+                    help="only time the vendor bf16 GEMM (torch.matmul, N x N x N) as a "
+                         "reference for the MFMA rate this chip sustains, and exit")
     return ap.parse_args()
 
 
@@ -246,6 +249,27 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_probe_bytes": n * 4}), flush=True)
+        return
+    if args.gemm_probe:
+        n = args.gemm_probe
+        g = torch.Generator(device="cuda").manual_seed(0)
+        a = torch.randn(n, n, device="cuda", dtype=torch.bfloat16, generator=g)
+        b = torch.randn(n, n, device="cuda", dtype=torch.bfloat16, generator=g)
+        for _ in range(5):
+            c = a @ b
+        torch.cuda.synchronize()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 20
+        ev0.record()
+        for _ in range(reps):
+            c = a @ b
+        ev1.record()
+        torch.cuda.synchronize()
+        ms = ev0.elapsed_time(ev1) / reps
+        tf = 2.0 * n ** 3 / (ms * 1e-3) / 1e12
+        print(json.dumps({"gemm_probe_n": n, "ms": round(ms, 4), "tflops": round(tf, 1),
+                          "pct_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2)}), flush=True)
+        del c
         return
     w = WORKLOADS[args.workload]
     precise = args.precise_ds if args.precise_ds >= 0 else (0 if args.workload in (4, 5) else 1)
