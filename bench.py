@@ -44,14 +44,14 @@ HBM_GBPS = 8000.0
 KERNEL_SOURCES = ["attn_bf16.hip", "attn_bf16.h", "attn_device.h", "attn_tiles.h",
                   "attn_internal.h", "attn_bwd_common.h", "attn_preprocess.hip"]
 MEASURED_TRAFFIC = {
-    ("18a2bebc18df7f69", 5, 0): {"attn_fwd": (231891 * 2.0 + 133950) * 1024,
+    ("1fdbbc3ba61ef9a6", 5, 0): {"attn_fwd": (236276 * 2.0 + 133767) * 1024,
                                  "attn_bwd_preprocess": (98333 * 2.0 + 4097) * 1024,
-                                 "attn_bwd_dkv_ds": (603207 * 2.0 + 8709541) * 1024,
-                                 "attn_bwd_dq_ds": (4310823 * 2.0 + 131081) * 1024},
-    ("18a2bebc18df7f69", 4, 0): {"attn_fwd": (465756 * 2.0 + 266241) * 1024,
-                                 "attn_bwd_preprocess": (196637 * 2.0 + 16403) * 1024,
-                                 "attn_bwd_dkv_ds": (1037800 * 2.0 + 6423378) * 1024,
-                                 "attn_bwd_dq_ds": (3557066 * 2.0 + 262153) * 1024},
+                                 "attn_bwd_dkv_ds": (361513 * 2.0 + 8683520) * 1024,
+                                 "attn_bwd_dq_ds": (4310540 * 2.0 + 131079) * 1024},
+    ("1fdbbc3ba61ef9a6", 4, 0): {"attn_fwd": (465728 * 2.0 + 266241) * 1024,
+                                 "attn_bwd_preprocess": (196637 * 2.0 + 16404) * 1024,
+                                 "attn_bwd_dkv_ds": (1034736 * 2.0 + 6423043) * 1024,
+                                 "attn_bwd_dq_ds": (3547964 * 2.0 + 262158) * 1024},
 }
 
 

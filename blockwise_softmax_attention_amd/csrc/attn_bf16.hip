@@ -699,8 +699,8 @@ __global__ __launch_bounds__(NTHREADS, 2) void dq_bf16_kernel(KArgs a) {
 // dS taken from the tiles the dK/dV kernel stored (WDS): no recomputation of
 // S, P or dP and no element work, so the kernel streams the stored tiles from
 // HBM.  Both operands reduce over keys and are read transposed from LDS
-// (ds_read_b64_tr_b16): the K tile (columns = d) and the key-major dS tile
-// (columns = queries; wave w takes its 32).
+// (ds_read_b64_tr_b16): the K tile (columns = d) and the dS tile in its
+// stored order (columns = queries; wave w takes its 32).
 //
 // A step covers DQS_BN keys of one listed tile (the visited key tiles are
 // listed once per workgroup).  With 32-key steps the rings take 72.7 KB, so
@@ -754,9 +754,7 @@ __global__ __launch_bounds__(NTHREADS, DQS_WG_PER_CU) void dq_ds_bf16_kernel(KAr
 
   const long kv_rs = (long)a.Hkv * D;
   const uint32_t kv_rsb = (uint32_t)(kv_rs * sizeof(bf16));
-  constexpr uint32_t S_RSB = DS_T * sizeof(bf16);
   const typename KT::Lane kln = KT::lane_of(kv_rsb, lane, wave);
-  const typename ST::Lane sln = ST::lane_of(S_RSB, lane, wave);
   const bf16* Kb = (const bf16*)a.k + ((long)b * L * a.Hkv + it.hkv) * D;
   const DsBand band = ds_band(L, a.causal, a.window);
   const int t_lo = ds_lo(qt, band), t_hi = ds_hi(qt, band);
@@ -800,11 +798,34 @@ __global__ __launch_bounds__(NTHREADS, DQS_WG_PER_CU) void dq_ds_bf16_kernel(KAr
     for (int i = 0; i < NK; ++i)
       KT::issue_one(lds_offset(sK[stg]), Kb + (long)kr0 * kv_rs, kv_rsb, L - kr0, kln, wave, i);
   };
+  // The dS ring holds each step's BN keys (BN / 32 groups of the stored
+  // tile, contiguous) as stored: 1 KB loads, LDS image = global image.
+  static_assert(BN % 32 == 0 && ST::BYTES == BN * DS_T * 2, "dS load pattern");
   auto issue_s = [&](int n, int stg) {
     const bf16* g = Sb + ((long)sList[n >> PSH] * DS_ELEMS + (long)(n & (PARTS - 1)) * BN * DS_T);
 #pragma unroll
-    for (int i = 0; i < NS; ++i)   // read once: non-temporal, K stays in L2
-      ST::template issue_one<true>(lds_offset(sS[stg]), g, S_RSB, BN, sln, wave, i);
+    for (int i = 0; i < NS; ++i) {   // read once: non-temporal, K stays in L2
+      const uint32_t j = (uint32_t)(wave + NWAVES * i);
+      const uint32_t m0 = (uint32_t)__builtin_amdgcn_readfirstlane(lds_offset(sS[stg]) + j * 1024);
+      dma16_nt(uniform_ptr(g), j * 1024 + 16 * (uint32_t)lane, m0);
+    }
+  };
+  // B operand of dQ^T += K^T dS^T for step t: this wave's 32 queries
+  // (columns) and the keys of K's LDS rows 16 t .. 16 t + 15 (rows; the K
+  // tile holds key pi32(x) in row x), gathered from the stored order by
+  // transposed reads (see BTile::tr_frag for the lane roles).
+  auto ds_frag = [&](const char* lds, int t) -> bf16x8 {
+    const int h = lane >> 5, mh = (lane >> 4) & 1, e = (lane & 15) >> 2, s = lane & 3;
+    const int c = 4 * wave + 2 * mh + (s >> 1);
+    const int r1 = 16 * t + 4 * h + e, r2 = r1 + 8;
+    const int k1 = (r1 & ~31) | pi32(r1 & 31), k2 = (r2 & ~31) | pi32(r2 & 31);
+    const char* a1 = lds + (k1 >> 5) * 8192 + ds_chunk_offset(k1 & 31, c) + ((s & 1) << 3);
+    const char* a2 = lds + (k2 >> 5) * 8192 + ds_chunk_offset(k2 & 31, c) + ((s & 1) << 3);
+    const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)a1);
+    const s16x4 v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)a2);
+    typedef short s16x8 __attribute__((ext_vector_type(8)));
+    const s16x8 v = {v1[0], v1[1], v1[2], v1[3], v2[0], v2[1], v2[2], v2[3]};
+    return __builtin_bit_cast(bf16x8, v);
   };
 
   f32x16 dqacc[NDB];
@@ -831,7 +852,7 @@ __global__ __launch_bounds__(NTHREADS, DQS_WG_PER_CU) void dq_ds_bf16_kernel(KAr
       const char* St = sS[ss];
 #pragma unroll
       for (int t = 0; t < BN / 16; ++t) {
-        const bf16x8 sf = ST::tr_frag(St, wave, t, lane);
+        const bf16x8 sf = ds_frag(St, t);
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
           const bf16x8 ka = KT::tr_frag(Kt, db, t, lane);
@@ -888,8 +909,8 @@ __device__ __forceinline__ void dkv_elementwise(f32x16 (&s)[NQB], f32x16 (&dp)[N
   }
 }
 
-// WDS: also store this step's bf16 dS, key-major, into the stored-dS
-// workspace (slot of block (query tile, key tile), see ds_slot), for the dQ
+// WDS: also store this step's bf16 dS, in the order of ds_chunk_offset, into
+// the stored-dS workspace (slot of block (query tile, key tile), see ds_slot), for the dQ
 // kernel of the stored-dS backward; the segment skip then takes the symmetric
 // test of segment_flags, which that kernel evaluates the same way.
 template <int D, int CAP, bool PRECISE, bool WDS>
@@ -1046,20 +1067,32 @@ __global__ __launch_bounds__(NTHREADS, 1) void dkv_bf16_kernel(KArgs a) {
 
   // Stored dS: lane (key kw0 + l32, half hh) holds, for query block qb, the
   // queries 32 qb + 16 h + 8 hh + 0..7 in its dS operand hi[h] (h = 0, 1):
-  // two 16-byte runs of its key's row of the key-major tile.
+  // query chunk c = 4 qb + 2 h + hh of its key, which ds_chunk_offset places
+  // so that each of the block's two stores writes 1 KB of whole lines.  The
+  // stores are non-temporal: the 8.6 GB dS stream of the long-context
+  // workload then no longer evicts from L2 the Q / dO tiles the XCD's other
+  // workgroups read again.
   const DsBand band = ds_band(L, a.causal, a.window);
-  const long ds_lane = (long)(wave * 32 + l32) * DS_T + 8 * hh;
+  const long ds_lane = (long)wave * 32 * DS_T + ds_chunk_offset(l32, hh) / 2;
+  // the second half's slot of this lane, relative to the first half's
+  const int ds_d1 = (ds_chunk_offset(l32, 2 + hh) - ds_chunk_offset(l32, hh)) / 2;
+  // Every visited block lies inside the band of stored tiles (the band comes
+  // from the same causal / window bounds that decide the visit), so the dS
+  // stores are unconditional: the compiler then counts them exactly in its
+  // vmcnt waits instead of assuming the worst over a branch.  (A slot outside
+  // the band, which no visited block has, would be clamped to the band's
+  // first tile, never written out of bounds.)
   auto ds_row = [&](int g, int t) -> bf16* {
     if (!WDS) return nullptr;
-    const long long slot = ds_slot(t, kt, band);
-    if (slot < 0) return nullptr;
+    long long slot = ds_slot(t, kt, band);
+    if (slot < 0) slot = 0;
     const long long head = (long long)b * a.Hq + hkv * G + g;
     return (bf16*)a.ds + (head * a.ds_slots + slot) * DS_ELEMS + ds_lane;
   };
   auto store_ds = [&](bf16* row, int qb, const bf16x8 (&hi)[2]) {
-    if (WDS && row != nullptr) {
-      *(bf16x8*)(row + 32 * qb) = hi[0];
-      *(bf16x8*)(row + 32 * qb + 16) = hi[1];
+    if (WDS) {
+      __builtin_nontemporal_store(hi[0], (bf16x8*)(row + 1024 * qb));
+      __builtin_nontemporal_store(hi[1], (bf16x8*)(row + 1024 * qb + ds_d1));
     }
   };
 
@@ -1212,6 +1245,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void dkv_bf16_kernel(KArgs a) {
       elementwise(s1, p1, qb);
       pack(s1[0], p1[0], pbp, hip, lop);
       store_ds(dsrow, qb, hip);
+      // the next step's constants, two blocks after their loads were sent
+      if (qb == 1 && more) store_consts(stg ^ 1);
     }
     // the last block's dV / dK
     {
@@ -1225,8 +1260,15 @@ __global__ __launch_bounds__(NTHREADS, 1) void dkv_bf16_kernel(KArgs a) {
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-    if (more) store_consts(stg ^ 1);
-    wait_vmcnt<0>();
+    if (NQB < 2 && more) store_consts(stg ^ 1);
+    // Vector memory operations complete in issue order, and the last block's
+    // two dS stores are the only ones issued after this step's last tile
+    // load: waiting down to two outstanding finds the next tiles in LDS
+    // without waiting for those stores to reach L2.
+    if (WDS)
+      wait_vmcnt<2>();
+    else
+      wait_vmcnt<0>();
     __syncthreads();
     stg ^= 1;
     gc = gn;

@@ -123,14 +123,28 @@ ATTN_HD bool query_tile_range(int k0, int k1, int bm, const MaskSpec& s, int* t0
 namespace attn {
 
 // Stored dS tiles.  The stored-dS backward keeps dS (bf16) of every visited
-// block of DS_T queries x DS_T keys, key-major (256 bytes per key for
-// DS_T = 128), so the dQ contraction can read it instead of recomputing it.
+// block of DS_T queries x DS_T keys, so the dQ contraction can read it
+// instead of recomputing it.  A tile is four 8 KB groups of 32 keys (the
+// keys of one dK/dV wave); a group is four 2 KB blocks of 32 queries, each
+// two 1 KB halves in the order the dK/dV wave holds them: 16-byte chunk
+// (key k, queries 8c .. 8c+7) of the group at byte ds_chunk_offset(k, c)
+// (c = 0 .. 15).  Each store instruction of that wave then writes 1 KB of
+// whole cache lines, and the dQ kernel loads a group with contiguous 1 KB
+// loads; the key bits XORed into a chunk's slot make the dQ kernel's
+// transposed LDS reads of it conflict-free on 64 banks (per 32 lanes).
 // Query tile qt of one (batch row, query head) owns the slots of its key-tile
 // band [ds_lo(qt), ds_hi(qt)), the key_tile_range of causal and window bounds
 // (identical for every batch row and head: ranker and segment skips only
 // leave slots unused), packed one query tile after another.
 constexpr int DS_T = 128;
 constexpr int DS_ELEMS = DS_T * DS_T;
+// Byte offset of chunk (key k, query chunk c) inside its 32-key group: block
+// c / 4 (2 KB each), half (c / 2) % 2 of it (1 KB: one store instruction),
+// then 16 bytes per slot 32 (c % 2) + (k ^ 4 (c % 2) ^ 8 ((c / 2) % 2)).
+ATTN_HD int ds_chunk_offset(int k, int c) {
+  const int pp = c & 1, hq = (c >> 1) & 1;
+  return (c >> 2) * 2048 + hq * 1024 + (pp * 32 + (k ^ (pp << 2) ^ (hq << 3))) * 16;
+}
 
 struct DsBand {
   int nt;       // tiles per side, ceil(L / DS_T)

@@ -181,7 +181,7 @@ attn_status attn_bwd_dkv(const attn_params* params, const void* q, const void* k
  *
  * Workspace: device memory of attn_bwd_ds_workspace_size() bytes, 16-byte
  * aligned, owned by the caller.  Layout (opaque to callers): per (batch row,
- * query head), one 128 x 128 bf16 tile (key-major) per block of 128 queries x
+ * query head), one 128 x 128 bf16 tile per block of 128 queries x
  * 128 keys inside the causal / window band of its query block; blocks with
  * no visible pair are neither written nor read.  Size: B * Hq * tiles * 32 KiB
  * with tiles = T (T + 1) / 2 for causal attention without a window,
