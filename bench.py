@@ -44,14 +44,14 @@ HBM_GBPS = 8000.0
 KERNEL_SOURCES = ["attn_bf16.hip", "attn_bf16.h", "attn_device.h", "attn_tiles.h",
                   "attn_internal.h", "attn_bwd_common.h", "attn_preprocess.hip"]
 MEASURED_TRAFFIC = {
-    ("1fdbbc3ba61ef9a6", 5, 0): {"attn_fwd": (236276 * 2.0 + 133767) * 1024,
+    ("5493ce4b0948f38b", 5, 0): {"attn_fwd": (230972 * 2.0 + 133921) * 1024,
                                  "attn_bwd_preprocess": (98333 * 2.0 + 4097) * 1024,
-                                 "attn_bwd_dkv_ds": (361513 * 2.0 + 8683520) * 1024,
-                                 "attn_bwd_dq_ds": (4310540 * 2.0 + 131079) * 1024},
-    ("1fdbbc3ba61ef9a6", 4, 0): {"attn_fwd": (465728 * 2.0 + 266241) * 1024,
-                                 "attn_bwd_preprocess": (196637 * 2.0 + 16404) * 1024,
-                                 "attn_bwd_dkv_ds": (1034736 * 2.0 + 6423043) * 1024,
-                                 "attn_bwd_dq_ds": (3547964 * 2.0 + 262158) * 1024},
+                                 "attn_bwd_dkv_ds": (361533 * 2.0 + 8683520) * 1024,
+                                 "attn_bwd_dq_ds": (4316608 * 2.0 + 131079) * 1024},
+    ("5493ce4b0948f38b", 4, 0): {"attn_fwd": (171861 * 2.0 + 269841) * 1024,
+                                 "attn_bwd_preprocess": (196638 * 2.0 + 16406) * 1024,
+                                 "attn_bwd_dkv_ds": (1034758 * 2.0 + 6423051) * 1024,
+                                 "attn_bwd_dq_ds": (3214598 * 2.0 + 262163) * 1024},
 }
 
 
