@@ -360,6 +360,28 @@ def test_gqa_ranker_general_bounds():
         check_tensor(n, got[n], ref[n], "f32")
 
 
+@pytest.mark.parametrize("B,Hq,Hkv,L", [(4, 4, 2, 1024),   # n_items a multiple of 8 B: rows ordered
+                                         (3, 2, 1, 300)])   # not: plain batch-row order
+def test_bf16_ranker_row_order(B, Hq, Hkv, L):
+    """The row kernels take the batch rows of a ranker workload longest history first
+    inside each XCD's run when the item count allows (ranker_row_order), else in the
+    plain order; both against the oracle, with history lengths that differ per row."""
+    w = dataclasses.replace(WORKLOADS[4].scaled(L=L, B=B, Hq=Hq, Hkv=Hkv), ranker=None)
+    inp = make_inputs(w)
+    # history lengths not sorted by row, so the longest-first order permutes the rows
+    h_len = [L // 3 + 37 * ((5 * b + 1) % B) for b in range(B)]
+    inp["ranker_bounds"] = torch.tensor([[0, h, h, L] for h in h_len], dtype=torch.int32)
+    say(f"[parity] bf16 ranker row order B{B} Hq{Hq} Hkv{Hkv} L{L} histories {h_len}")
+    for precise in (False, True):
+        got = run_gpu(w, inp, precise)
+        hin = host_inputs(inp)
+        ref = backward(hin["q"], hin["k"], hin["v"], hin["do"], oracle_params(w), hin["temp"],
+                       hin["seg"], hin["rb"])
+        check_ml(got["m"], got["l"], ref["m"], ref["l"], "bf16")
+        for n in ("o", "dq", "dk", "dv"):
+            check_tensor(n, got[n], ref[n], "bf16")
+
+
 def test_deterministic():
     w = REDUCED[4]
     inp = make_inputs(w)
