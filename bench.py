@@ -90,6 +90,9 @@ def parse():
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (HBM counter "
                          "calibration) and exit")
+    ap.add_argument("--hbm-probe", type=int, default=0, metavar="MIB",
+                    help="only time torch's own streaming kernels (sum, copy, fill) on MIB MiB "
+                         "as a reference for the HBM rate this chip sustains, and exit")
     ap.add_argument("--gemm-probe", type=int, default=0, metavar="N",
                     help="only time the vendor bf16 GEMM (torch.matmul, N x N x N) as a "
                          "reference for the MFMA rate this chip sustains, and exit")
@@ -249,6 +252,29 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_probe_bytes": n * 4}), flush=True)
+        return
+    if args.hbm_probe:
+        n = args.hbm_probe * (1 << 20) // 4
+        x = torch.ones(n, dtype=torch.float32, device="cuda")
+        y = torch.empty_like(x)
+
+        def rate(fn, nbytes, reps=10):
+            for _ in range(3):
+                fn()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / reps
+            return {"ms": round(ms, 4), "tb_per_s": round(nbytes / (ms * 1e-3) / 1e12, 2)}
+
+        print(json.dumps({"hbm_probe_bytes": n * 4,
+                          "sum_read": rate(lambda: x.sum(), n * 4),
+                          "copy_read_write": rate(lambda: y.copy_(x), 2 * n * 4),
+                          "fill_write": rate(lambda: y.fill_(1.0), n * 4)}), flush=True)
         return
     if args.gemm_probe:
         n = args.gemm_probe
