@@ -44,23 +44,26 @@ HBM_GBPS = 8000.0
 KERNEL_SOURCES = ["attn_bf16.hip", "attn_bf16.h", "attn_device.h", "attn_tiles.h",
                   "attn_internal.h", "attn_bwd_common.h", "attn_preprocess.hip"]
 MEASURED_TRAFFIC = {
-    ("5493ce4b0948f38b", 5, 0): {"attn_fwd": (230972 * 2.0 + 133921) * 1024,
-                                 "attn_bwd_preprocess": (98333 * 2.0 + 4097) * 1024,
-                                 "attn_bwd_dkv_ds": (361533 * 2.0 + 8683520) * 1024,
-                                 "attn_bwd_dq_ds": (4316608 * 2.0 + 131079) * 1024},
-    ("5493ce4b0948f38b", 4, 0): {"attn_fwd": (171861 * 2.0 + 269841) * 1024,
-                                 "attn_bwd_preprocess": (196638 * 2.0 + 16406) * 1024,
-                                 "attn_bwd_dkv_ds": (1034758 * 2.0 + 6423051) * 1024,
-                                 "attn_bwd_dq_ds": (3214598 * 2.0 + 262163) * 1024},
+    ("2e3d7b799bb769c4", 5, 0): {"attn_fwd": (230498 * 2.0 + 134128) * 1024,
+                                 "attn_bwd_preprocess": (98333 * 2.0 + 4096) * 1024,
+                                 "attn_bwd_dkv_ds": (361597 * 2.0 + 8683526) * 1024,
+                                 "attn_bwd_dq_ds": (4314845 * 2.0 + 131081) * 1024},
+    ("2e3d7b799bb769c4", 4, 0): {"attn_fwd": (171887 * 2.0 + 270316) * 1024,
+                                 "attn_bwd_preprocess": (196637 * 2.0 + 16401) * 1024,
+                                 "attn_bwd_dkv_ds": (1034910 * 2.0 + 6423220) * 1024,
+                                 "attn_bwd_dq_ds": (3215043 * 2.0 + 262162) * 1024},
 }
 
 
 def kernel_source_hash() -> str:
-    """Hash of the kernel sources' code: comments and whitespace are dropped,
-    so an edited comment keeps the measured traffic, a changed kernel not."""
+    """Hash of the kernel sources' code and their per-source compiler flags:
+    comments and whitespace are dropped, so an edited comment keeps the
+    measured traffic, a changed kernel not."""
     import hashlib
     import re
+    from blockwise_softmax_attention_amd.build import SOURCE_FLAGS
     h = hashlib.sha256()
+    h.update(repr(sorted(SOURCE_FLAGS.items())).encode())
     for f in KERNEL_SOURCES:
         with open(os.path.join(ROOT, "blockwise_softmax_attention_amd", "csrc", f)) as fh:
             src = fh.read()

@@ -50,9 +50,6 @@
 #ifndef ATTN_PRIO
 #define ATTN_PRIO 1
 #endif
-#ifndef ATTN_DKV_PIN
-#define ATTN_DKV_PIN 1
-#endif
 
 
 namespace attn {
@@ -947,6 +944,55 @@ __device__ __forceinline__ void dkv_elementwise(f32x16 (&s)[NQB], f32x16 (&dp)[N
   }
 }
 
+// One dV / dK unit: dv += oa x pb, dk += qa x hi (and + qa x lo with the
+// split dS), in one asm block so that the two accumulators stay in AGPRs
+// while the S / dP chains of the same loop use the VGPR form of the MFMA
+// (this source is built with that form as the default).  Left to the compiler,
+// the dK / dV accumulators were moved between the two register files on every
+// step.  The compiler does not see into the block, so it carries its own wait
+// states: an operand written by a VALU instruction (the bf16 packing, or the
+// zeroing of an accumulator) needs two before an MFMA reads it, which the
+// leading s_nop 1 gives; the dK MFMA that follows overwrites exactly its own
+// srcC with the same opcode and needs none.  The accumulators are read only
+// after the step loop, behind dkv_acc_fence.
+template <bool PRECISE>
+__device__ __forceinline__ void dvdk_mfma(f32x16& dv, f32x16& dk, const bf16x8& oa, const bf16x8& pb,
+                                          const bf16x8& qa, const bf16x8& hi, const bf16x8& lo) {
+  if (PRECISE) {
+    asm volatile(
+        "s_nop 1\n\t"
+        "v_mfma_f32_32x32x16_bf16 %0, %2, %3, %0\n\t"
+        "v_mfma_f32_32x32x16_bf16 %1, %4, %5, %1\n\t"
+        "v_mfma_f32_32x32x16_bf16 %1, %4, %6, %1"
+        : "+a"(dv), "+a"(dk)
+        : "v"(oa), "v"(pb), "v"(qa), "v"(hi), "v"(lo));
+  } else {
+    asm volatile(
+        "s_nop 1\n\t"
+        "v_mfma_f32_32x32x16_bf16 %0, %2, %3, %0\n\t"
+        "v_mfma_f32_32x32x16_bf16 %1, %4, %5, %1"
+        : "+a"(dv), "+a"(dk)
+        : "v"(oa), "v"(pb), "v"(qa), "v"(hi));
+  }
+}
+
+// Before anything reads an accumulator that dvdk_mfma wrote: an MFMA result
+// read by a VALU or memory instruction needs up to about a dozen wait states;
+// the first block gives 24.  Each accumulator then passes through an empty
+// block of its own, ordered after the first, so that no read of it can be
+// scheduled above the wait.  (One block with all of them as operands made the
+// register allocator copy them between AGPRs first, reads the wait would not
+// cover.)
+template <int NDB>
+__device__ __forceinline__ void dkv_acc_fence(f32x16 (&dk)[NDB], f32x16 (&dv)[NDB]) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+#pragma unroll
+  for (int i = 0; i < NDB; ++i) {
+    asm volatile("" : "+a"(dk[i]));
+    asm volatile("" : "+a"(dv[i]));
+  }
+}
+
 // WDS: also store this step's bf16 dS, in the order of ds_chunk_offset, into
 // the stored-dS workspace (slot of block (query tile, key tile), see ds_slot), for the dQ
 // kernel of the stored-dS backward; the segment skip then takes the symmetric
@@ -1101,7 +1147,14 @@ __global__ __launch_bounds__(NTHREADS, 1) void dkv_bf16_kernel(KArgs a) {
 
   f32x16 dkacc[NDB], dvacc[NDB];
 #pragma unroll
-  for (int i = 0; i < NDB; ++i) dkacc[i] = dvacc[i] = f32x16{};
+  for (int i = 0; i < NDB; ++i) {
+    dkacc[i] = dvacc[i] = f32x16{};
+    // zeroed once, in the AGPRs the MFMAs accumulate into (a constant would be
+    // rematerialised on the path that skips the step loop, and the two paths
+    // then merged by copies between AGPRs after the loop)
+    asm volatile("" : "+a"(dkacc[i]));
+    asm volatile("" : "+a"(dvacc[i]));
+  }
 
   // Stored dS: lane (key kw0 + l32, half hh) holds, for query block qb, the
   // queries 32 qb + 16 h + 8 hh + 0..7 in its dS operand hi[h] (h = 0, 1):
@@ -1191,9 +1244,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void dkv_bf16_kernel(KArgs a) {
     auto dvdk_unit = [&](int u, const bf16x8 (&pb)[2], const bf16x8 (&hi)[2], const bf16x8 (&lo)[2],
                          const bf16x8& oa, const bf16x8& qa) {
       const int h = u / NDB, db = u % NDB;
-      dvacc[db] = Elem<bf16>::mfma(oa, pb[h], dvacc[db]);
-      dkacc[db] = Elem<bf16>::mfma(qa, hi[h], dkacc[db]);
-      if (PRECISE) dkacc[db] = Elem<bf16>::mfma(qa, lo[h], dkacc[db]);
+      dvdk_mfma<PRECISE>(dvacc[db], dkacc[db], oa, pb[h], qa, hi[h], lo[h]);
     };
     auto tr_pair = [&](int qb, int u, bf16x8& oa, bf16x8& qa) {
       const int h = u / NDB, db = u % NDB, tt = 2 * qb + h;
@@ -1228,14 +1279,6 @@ __global__ __launch_bounds__(NTHREADS, 1) void dkv_bf16_kernel(KArgs a) {
         }
         s0[0] = Elem<bf16>::mfma(fq[cur], kf[t], s0[0]);
         p0[0] = Elem<bf16>::mfma(fo[cur], vf[t], p0[0]);
-#if ATTN_DKV_PIN
-        // the dK/dV accumulators stay in AGPRs across this chain (left free,
-        // the allocator parks 32 of them in VGPRs and moves them back each step)
-        if (t == 0 || t == NT16 - 1) {
-#pragma unroll
-          for (int i = 0; i < NDB; ++i) asm volatile("" : "+a"(dkacc[i]), "+a"(dvacc[i]));
-        }
-#endif
         if (t + 1 < NT16) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
         __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
         dma(0, t);
@@ -1314,6 +1357,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void dkv_bf16_kernel(KArgs a) {
     have = more;
   }
 
+  dkv_acc_fence(dkacc, dvacc);
   if (key_ok) {
     float* dkrow = a.out0 + ((long)(b * L + krow) * a.Hkv + hkv) * D;
     float* dvrow = a.out1 + ((long)(b * L + krow) * a.Hkv + hkv) * D;
