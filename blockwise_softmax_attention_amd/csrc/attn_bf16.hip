@@ -24,8 +24,7 @@
 #include "attn_bwd_common.h"
 
 // Per-kernel build choices: tile sizes, occupancy of the forward, address
-// laundering (see BTile), the MFMA-burst priority (mfma_phase) and the AGPR
-// pins of the dK/dV accumulators.
+// laundering (see BTile) and the MFMA-burst priority (mfma_phase).
 #ifndef ATTN_LAUNDER_FWD
 #define ATTN_LAUNDER_FWD 0
 #endif
@@ -54,7 +53,9 @@
 
 namespace attn {
 
-constexpr int BN16 = ATTN_FWD_BN;   // keys per tile (forward)
+constexpr int BN16 = ATTN_FWD_BN;
+constexpr int DKV_PLAN_MAX = 2048;   // dK/dV step-plan entries (query tiles per key block)
+static_assert(DKV_PLAN_MAX * ATTN_DKV_BQ >= ATTN_MAX_SEQ_LEN, "a plan entry for every query tile");   // keys per tile (forward)
 constexpr int BNQ16 = ATTN_DQ_BN;   // keys per tile (dQ: Q and dO fragments stay in registers)
 constexpr int BQ16 = ATTN_DKV_BQ;   // queries per tile (dK/dV)
 constexpr float RESCALE_TAU = 8.f;
@@ -1016,6 +1017,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void dkv_bf16_kernel(KArgs a) {
   __shared__ unsigned char sMixed[MAX_TILES];
   __shared__ unsigned char sFlag2[WDS ? MAX_TILES : 1];
   __shared__ int sRange[2];
+  __shared__ int sPlan[DKV_PLAN_MAX];
+  __shared__ int sPlanN;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1058,31 +1061,39 @@ __global__ __launch_bounds__(NTHREADS, 1) void dkv_bf16_kernel(KArgs a) {
   const bool any = query_tile_range(k0, k1, BQ, ms, &t_lo, &t_hi);
   if (has_seg && any)
     segment_flags(segb, k0, k1, t_lo, t_hi, BQ, L, tid, sFlag, sMixed, sRange, WDS ? sFlag2 : nullptr);
-  auto next_needed = [&](int t) -> int {
-    for (; t < t_hi; ++t) {
-      if (tile_class(t * BQ, t * BQ + BQ, k0, k1, ms) == TILE_EMPTY) continue;
-      if (has_seg && !(sFlag[t - t_lo] && (!WDS || sFlag2[t - t_lo]))) continue;
-      return t;
-    }
-    return -1;
-  };
-  auto next_step = [&](int g, int t, int& gn, int& tn) -> bool {
-    int x = next_needed(t + 1);
-    if (x >= 0) {
-      gn = g;
-      tn = x;
-      return true;
-    }
-    if (g + 1 < G) {
-      x = next_needed(t_lo);
-      if (x >= 0) {
-        gn = g + 1;
-        tn = x;
-        return true;
+  // The step plan: the query tiles this key block visits, in order, each with
+  // the tile class every wave's 32 keys see, built once by wave 0 (one
+  // ballot per 64 tiles), so that a step only reads its entry.  The steps
+  // are the plan's tiles for each group head in turn.  Entry: tile index
+  // (bits 0-15), then 2 bits of class per wave.
+  if (wave == 0) {
+    int cnt = 0;
+    if (any) {
+      for (int t0 = t_lo; t0 < t_hi; t0 += 64) {
+        const int t = t0 + lane;
+        bool vis = t < t_hi && tile_class(t * BQ, t * BQ + BQ, k0, k1, ms) != TILE_EMPTY;
+        if (vis && has_seg) vis = sFlag[t - t_lo] && (!WDS || sFlag2[t - t_lo]);
+        int e = t;
+        if (vis) {
+          MaskSpec mt = ms;
+          if (ms.has_seg && sRange[0] == sRange[1] && !sMixed[t - t_lo]) mt.has_seg = false;
+#pragma unroll
+          for (int w = 0; w < NWAVES; ++w)
+            e |= tile_class(t * BQ, t * BQ + BQ, k0 + 32 * w, k0 + 32 * w + 32, mt) << (16 + 2 * w);
+        }
+        const uint64_t m = __ballot(vis);
+        const int pos = cnt + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                             __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
+        if (vis && pos < DKV_PLAN_MAX) sPlan[pos] = e;
+        cnt += __builtin_popcountll(m);
       }
     }
-    return false;
-  };
+    if (lane == 0) sPlanN = cnt;
+  }
+  __syncthreads();
+  // (never above DKV_PLAN_MAX while L <= ATTN_MAX_SEQ_LEN; clamped all the same)
+  const int nplan = imin(__builtin_amdgcn_readfirstlane(sPlanN), DKV_PLAN_MAX);
+  auto plan_entry = [&](int i) -> int { return __builtin_amdgcn_readfirstlane(sPlan[i]); };
   // Per-query inputs of the next step (m, l, delta, temperature, segment id):
   // each wave loads BQ / NWAVES of them into registers when the step's tile
   // loads are issued, and derives the constants from them only after the
@@ -1187,8 +1198,33 @@ __global__ __launch_bounds__(NTHREADS, 1) void dkv_bf16_kernel(KArgs a) {
     }
   };
 
-  int gc = 0, tc = any ? next_needed(t_lo) : -1;
+  // A step is (group head g, plan index p, entry e).  The step after (g, p):
+  // the next entry, or the first one for the next group head; false past the
+  // last head.  Branch-free, so that it runs beside the MFMAs of block 1.
+  auto advance = [&](int g, int p, int& g2, int& p2, int& e2) -> bool {
+    const bool wrap = p + 1 == nplan;
+    p2 = wrap ? 0 : p + 1;
+    g2 = wrap ? g + 1 : g;
+    e2 = plan_entry(p2);
+    return g2 < G;
+  };
+  int gc = 0, pc = 0, ec = 0, tc = -1;
+  if (nplan > 0) {
+    ec = plan_entry(0);
+    tc = ec & 0xffff;
+  }
   bool have = tc >= 0;
+  // the next step; without one, the loads of the last step refetch its own
+  // tile into the idle stage (branch-free loop body; once per work-group)
+  int gn = gc, pn = pc, en = ec;
+  bool more = have && advance(gc, pc, gn, pn, en);
+  if (!more) {
+    gn = gc;
+    pn = pc;
+    en = ec;
+  }
+  int tn = en & 0xffff;
+  bf16* dsrow = have ? ds_row(gc, tc) : nullptr;
   if (have) {
     issue(gc, tc, 0);
     fetch_consts(gc, tc);
@@ -1198,21 +1234,17 @@ __global__ __launch_bounds__(NTHREADS, 1) void dkv_bf16_kernel(KArgs a) {
   __syncthreads();
   int stg = 0;
   while (have) {
-    int gn = gc, tn = tc;
-    // without a next step, the loads below refetch the current tile into the
-    // idle stage (branch-free loop body; once per work-group)
-    const bool more = next_step(gc, tc, gn, tn);
-    if (!more) {
-      gn = gc;
-      tn = tc;
-    }
     const int q0 = tc * BQ;
-    bf16* const dsrow = ds_row(gc, tc);
+    // the step after the next and the next step's dS row, worked out during
+    // block 1 (scalar work beside its MFMAs, ready when the next step starts)
+    int g2 = gn, p2 = pn, e2 = en;
+    bool more2 = false;
+    bf16* dsrow_n = dsrow;
     const char* Qt = sQ[stg];
     const char* Ot = sO[stg];
     // the tile class is the same on every lane; readfirstlane lets the compiler
     // branch on it instead of running every variant under an exec mask
-    const int tcls = seg_tile_class(q0, q0 + BQ, kw0, kw0 + 32, ms, tc, t_lo, sMixed, sRange);
+    const int tcls = (ec >> (16 + 2 * wave)) & 3;
     auto elementwise = [&](f32x16 (&sa)[1], f32x16 (&pa)[1], int qb) {
       const int o = 32 * qb;
       if (tcls == TILE_FULL) {
@@ -1253,6 +1285,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void dkv_bf16_kernel(KArgs a) {
     };
     constexpr int NU = 2 * NDB;   // dV / dK units per block
     static_assert(NU == NT16 || NU * 2 == NT16, "units per reduction step");
+    static_assert(NQB >= 2, "the next step is worked out during block 1");
     constexpr int UPT = NU / NT16 > 0 ? NU / NT16 : 1;   // units per S/dP reduction step
     constexpr int TPU = NT16 / NU > 0 ? NT16 / NU : 1;   // reduction steps per unit
     // this step's tile loads, spread over the reduction steps of all blocks
@@ -1304,6 +1337,11 @@ __global__ __launch_bounds__(NTHREADS, 1) void dkv_bf16_kernel(KArgs a) {
 #pragma unroll
         for (int t = 0; t < NT16; ++t) {
           const int cur = t & 1;
+          if (qb == 1 && t == 0) {
+            // (also on the last step, where its result is not used)
+            more2 = advance(gn, pn, g2, p2, e2) & more;
+            dsrow_n = ds_row(gn, tn);
+          }
           if (t + 1 < NT16) {
             fq[cur ^ 1] = QT::row_frag(Qt, qb, t + 1, lane);
             fo[cur ^ 1] = QT::row_frag(Ot, qb, t + 1, lane);
@@ -1354,7 +1392,21 @@ __global__ __launch_bounds__(NTHREADS, 1) void dkv_bf16_kernel(KArgs a) {
     stg ^= 1;
     gc = gn;
     tc = tn;
+    pc = pn;
+    ec = en;
+    dsrow = dsrow_n;
     have = more;
+    more = more2;
+    if (more) {
+      gn = g2;
+      pn = p2;
+      en = e2;
+    } else {
+      gn = gc;
+      pn = pc;
+      en = ec;
+    }
+    tn = en & 0xffff;
   }
 
   dkv_acc_fence(dkacc, dvacc);
