@@ -827,8 +827,9 @@ __global__ __launch_bounds__(NTHREADS, DQS_WG_PER_CU) void dq_ds_bf16_kernel(KAr
   const int last = ntiles > 0 ? t_lo + sList[ntiles - 1] : 0;
   const int last_parts = imin(PARTS, (L - last * DS_T + BN - 1) / BN);
   const int nsteps = ntiles > 0 ? PARTS * (ntiles - 1) + last_parts : 0;
-  auto issue_k = [&](int n, int stg) {
-    const int kt = t_lo + sList[n >> PSH];
+  // (e: the list entry of step n, sList[n >> PSH])
+  auto issue_k = [&](int n, int stg, int e) {
+    const int kt = t_lo + e;
     const int kr0 = kt * DS_T + (n & (PARTS - 1)) * BN;
 #pragma unroll
     for (int i = 0; i < NK; ++i)
@@ -837,8 +838,8 @@ __global__ __launch_bounds__(NTHREADS, DQS_WG_PER_CU) void dq_ds_bf16_kernel(KAr
   // The dS ring holds each step's BN keys (BN / 32 groups of the stored
   // tile, contiguous) as stored: 1 KB loads, LDS image = global image.
   static_assert(BN % 32 == 0 && ST::BYTES == BN * DS_T * 2, "dS load pattern");
-  auto issue_s = [&](int n, int stg) {
-    const bf16* g = Sb + ((long)sList[n >> PSH] * DS_ELEMS + (long)(n & (PARTS - 1)) * BN * DS_T);
+  auto issue_s = [&](int n, int stg, int e) {
+    const bf16* g = Sb + ((long)e * DS_ELEMS + (long)(n & (PARTS - 1)) * BN * DS_T);
 #pragma unroll
     for (int i = 0; i < NS; ++i) {   // read once: non-temporal, K stays in L2
       const uint32_t j = (uint32_t)(wave + NWAVES * i);
@@ -872,18 +873,24 @@ __global__ __launch_bounds__(NTHREADS, DQS_WG_PER_CU) void dq_ds_bf16_kernel(KAr
     // prologue: dS(0 .. SST-4), K(0), dS(SST-3), K(1), dS(SST-2); step
     // numbers past the last step repeat the last one
     const int nl = nsteps - 1;
+    auto entry = [&](int n) -> int { return sList[n >> PSH]; };
 #pragma unroll
-    for (int n = 0; n < SST - 3; ++n) issue_s(imin(n, nl), n);
-    issue_k(0, 0);
-    issue_s(imin(SST - 3, nl), SST - 3);
-    issue_k(imin(1, nl), 1);
-    issue_s(imin(SST - 2, nl), SST - 2);
+    for (int n = 0; n < SST - 3; ++n) issue_s(imin(n, nl), n, entry(imin(n, nl)));
+    issue_k(0, 0, entry(0));
+    issue_s(imin(SST - 3, nl), SST - 3, entry(imin(SST - 3, nl)));
+    issue_k(imin(1, nl), 1, entry(imin(1, nl)));
+    issue_s(imin(SST - 2, nl), SST - 2, entry(imin(SST - 2, nl)));
+    // the list entries of the next step's loads, read one step ahead so that
+    // their LDS latency passes during a step's MFMAs
+    int ek = entry(imin(2, nl)), es = entry(imin(SST - 1, nl));
     int ks = 0, ss = 0;   // stages of the current step
     for (int n = 0; n < nsteps; ++n) {
       wait_vmcnt<2 * NS + NK>();
       __syncthreads();
-      issue_k(imin(n + 2, nl), ks == 0 ? 2 : ks - 1);
-      issue_s(imin(n + SST - 1, nl), ss == 0 ? SST - 1 : ss - 1);
+      issue_k(imin(n + 2, nl), ks == 0 ? 2 : ks - 1, ek);
+      issue_s(imin(n + SST - 1, nl), ss == 0 ? SST - 1 : ss - 1, es);
+      ek = entry(imin(n + 3, nl));
+      es = entry(imin(n + SST, nl));
       const char* Kt = sK[ks];
       const char* St = sS[ss];
 #pragma unroll
