@@ -44,14 +44,14 @@ HBM_GBPS = 8000.0
 KERNEL_SOURCES = ["attn_bf16.hip", "attn_bf16.h", "attn_device.h", "attn_tiles.h",
                   "attn_internal.h", "attn_bwd_common.h", "attn_preprocess.hip"]
 MEASURED_TRAFFIC = {
-    ("2e3d7b799bb769c4", 5, 0): {"attn_fwd": (230498 * 2.0 + 134128) * 1024,
+    ("529d0ac48c0989ed", 5, 0): {"attn_fwd": (232048 * 2.0 + 134221) * 1024,
                                  "attn_bwd_preprocess": (98333 * 2.0 + 4096) * 1024,
-                                 "attn_bwd_dkv_ds": (361597 * 2.0 + 8683526) * 1024,
-                                 "attn_bwd_dq_ds": (4314845 * 2.0 + 131081) * 1024},
-    ("2e3d7b799bb769c4", 4, 0): {"attn_fwd": (171887 * 2.0 + 270316) * 1024,
-                                 "attn_bwd_preprocess": (196637 * 2.0 + 16401) * 1024,
-                                 "attn_bwd_dkv_ds": (1034910 * 2.0 + 6423220) * 1024,
-                                 "attn_bwd_dq_ds": (3215043 * 2.0 + 262162) * 1024},
+                                 "attn_bwd_dkv_ds": (361786 * 2.0 + 8683520) * 1024,
+                                 "attn_bwd_dq_ds": (4313000 * 2.0 + 131079) * 1024},
+    ("529d0ac48c0989ed", 4, 0): {"attn_fwd": (171893 * 2.0 + 270336) * 1024,
+                                 "attn_bwd_preprocess": (196637 * 2.0 + 16404) * 1024,
+                                 "attn_bwd_dkv_ds": (1036245 * 2.0 + 6423047) * 1024,
+                                 "attn_bwd_dq_ds": (3210027 * 2.0 + 262162) * 1024},
 }
 
 
@@ -96,6 +96,10 @@ def parse():
     ap.add_argument("--hbm-probe", type=int, default=0, metavar="MIB",
                     help="only time torch's own streaming kernels (sum, copy, fill) on MIB MiB "
                          "as a reference for the HBM rate this chip sustains, and exit")
+    ap.add_argument("--stream-probe", type=int, default=0, metavar="MIB",
+                    help="only time attn_probe_stream (the kernels' direct-to-LDS loads "
+                         "streaming MIB MiB from HBM) as a reference for the read rate "
+                         "those loads reach, and exit")
     ap.add_argument("--gemm-probe", type=int, default=0, metavar="N",
                     help="only time the vendor bf16 GEMM (torch.matmul, N x N x N) as a "
                          "reference for the MFMA rate this chip sustains, and exit")
@@ -278,6 +282,28 @@ def main():
                           "sum_read": rate(lambda: x.sum(), n * 4),
                           "copy_read_write": rate(lambda: y.copy_(x), 2 * n * 4),
                           "fill_write": rate(lambda: y.fill_(1.0), n * 4)}), flush=True)
+        return
+    if args.stream_probe:
+        nbytes = args.stream_probe * (1 << 20)
+        src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+        res = {"stream_probe_bytes": nbytes}
+        for blocks in (512, 1024, 2048, 4096):
+            if nbytes % (1024 * blocks):
+                continue
+            out = torch.empty(blocks, dtype=torch.float32, device="cuda")
+            for _ in range(3):
+                ba.attn_probe_stream(src, blocks, out)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            reps = 10
+            e0.record()
+            for _ in range(reps):
+                ba.attn_probe_stream(src, blocks, out)
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / reps
+            res[f"blocks_{blocks}"] = {"ms": round(ms, 4), "tb_per_s": round(nbytes / (ms * 1e-3) / 1e12, 2)}
+        print(json.dumps(res), flush=True)
         return
     if args.gemm_probe:
         n = args.gemm_probe

@@ -8,7 +8,7 @@ missing or the tensors are not on the GPU, the calls raise.
 Names mirror the C ABI: attn_fwd, attn_bwd_preprocess, attn_bwd_dq,
 attn_bwd_dkv, attn_bwd_ds_workspace_size, attn_bwd_dkv_ds, attn_bwd_dq_ds,
 attn_bwd_ds_static, attn_reduce_heads, attn_ranker_bounds, attn_plan_count,
-attn_check_params.
+attn_check_params, and the measurement helper attn_probe_stream.
 """
 from __future__ import annotations
 
@@ -79,6 +79,7 @@ _FN_SIGS = {
     "attn_bwd_dq": [ctypes.POINTER(_CParams), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
     "attn_reduce_heads": [ctypes.POINTER(_CParams), _P, _P, _P],
     "attn_ranker_bounds": [_P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P, _P],
+    "attn_probe_stream": [_P, ctypes.c_int64, ctypes.c_int32, _P, _P],
     "attn_bwd_dkv": [ctypes.POINTER(_CParams), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
     "attn_plan_count": [ctypes.POINTER(_CParams), _P, _P, ctypes.POINTER(ctypes.c_int64),
                         ctypes.POINTER(ctypes.c_int64)],
@@ -213,6 +214,19 @@ def attn_ranker_bounds(segment_ids, history_id: int, candidate_id: int, out=None
     _check(load_library().attn_ranker_bounds(
         _ptr(segment_ids, "segment_ids", torch.int32), int(B), int(L), int(history_id),
         int(candidate_id), _ptr(out, "ranker_bounds", torch.int32), _stream(stream)))
+    return out
+
+
+def attn_probe_stream(src, blocks: int, out=None, stream=None):
+    """Measurement helper: blocks work-groups stream src (a contiguous device
+    tensor, nbytes a multiple of 1024 * blocks) into LDS with the kernels'
+    direct-to-LDS loads; out (blocks,) float32 gets the first float of each
+    slice's last 1 KB."""
+    if not src.is_contiguous():
+        raise ValueError("src must be contiguous")
+    out = torch.empty((blocks,), dtype=torch.float32, device=src.device) if out is None else out
+    _check(load_library().attn_probe_stream(_ptr(src, "src"), int(src.numel() * src.element_size()),
+                                            int(blocks), _ptr(out, "out", torch.float32), _stream(stream)))
     return out
 
 

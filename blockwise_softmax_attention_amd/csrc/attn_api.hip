@@ -292,6 +292,16 @@ attn_status attn_reduce_heads(const attn_params* p, const float* x, float* out, 
                     "attn_reduce_heads launch");
 }
 
+attn_status attn_probe_stream(const void* src, int64_t bytes, int32_t blocks, float* out, void* stream) {
+  if (blocks < 1 || blocks > 65536) return fail(ATTN_ERR_SHAPE, "blocks must be in [1, 65536]");
+  if (bytes < 1 || bytes % (1024LL * blocks) != 0)
+    return fail(ATTN_ERR_SHAPE, "bytes must be a positive multiple of 1024 * blocks");
+  ATTN_TRY(check_ptr(src, "src", 16));
+  ATTN_TRY(check_ptr(out, "out", 4));
+  return hip_status(attn::launch_stream_probe(src, (long long)bytes, blocks, out, (hipStream_t)stream),
+                    "attn_probe_stream launch");
+}
+
 attn_status attn_ranker_bounds(const int32_t* segment_ids, int32_t batch, int32_t seq_len,
                                int32_t history_id, int32_t candidate_id, int32_t* ranker_bounds,
                                void* stream) {

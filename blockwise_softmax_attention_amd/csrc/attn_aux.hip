@@ -11,8 +11,15 @@
 // page, test harness: the ranker's history and candidate rows are marked by
 // two reserved segment ids; the page prints neither the values nor the
 // mapping, so both ids are arguments and the interval is this reading.)
+//
+// stream_probe: a read-rate reference, not part of attention.  Each
+// work-group reads its own contiguous slice of src with the direct-to-LDS,
+// non-temporal 16-byte loads the kernels use (1 KB per wave instruction, at
+// most 8 in flight per wave) into a 64 KB LDS ring that nothing else reads,
+// then writes the first float of its slice's last 1 KB to out[block].
 #include "attn_internal.h"
 #include "attn_tiles.h"
+#include "attn_bf16.h"
 
 namespace attn {
 
@@ -70,6 +77,34 @@ __global__ __launch_bounds__(256) void ranker_bounds_kernel(const int32_t* __res
     bounds[4 * b + 2] = c ? r_cmin[0] : 0;
     bounds[4 * b + 3] = c ? r_cmax[0] + 1 : 0;
   }
+}
+
+__global__ __launch_bounds__(256) void stream_probe_kernel(const char* __restrict__ src, long long per_wg,
+                                                           float* __restrict__ out) {
+  __shared__ __attribute__((aligned(1024))) char ring[64 * 1024];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const char* base = src + blockIdx.x * per_wg;
+  const long long nchunks = per_wg / 1024;
+  const uint32_t ring0 = lds_offset(ring);
+  for (long long c = wave; c < nchunks; c += 4) {
+    // slot (wave, (c / 4) % 16): 16 KB of the ring per wave
+    const uint32_t m0 = (uint32_t)__builtin_amdgcn_readfirstlane(ring0 + (uint32_t)(wave * 16 + ((c >> 2) & 15)) * 1024u);
+    dma16_nt(uniform_ptr(base + c * 1024), 16u * (uint32_t)lane, m0);
+    wait_vmcnt<8>();
+  }
+  wait_vmcnt<0>();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const long long c = nchunks - 1;
+    const int w = (int)(c & 3);
+    out[blockIdx.x] = *(const float*)(ring + (w * 16 + ((c >> 2) & 15)) * 1024);
+  }
+}
+
+hipError_t launch_stream_probe(const void* src, long long bytes, int blocks, float* out, hipStream_t s) {
+  hipLaunchKernelGGL(stream_probe_kernel, dim3(blocks), dim3(256), 0, s, (const char*)src,
+                     bytes / blocks, out);
+  return hipGetLastError();
 }
 
 hipError_t launch_reduce_heads(const float* x, float* out, int B, int H, int L, hipStream_t s) {

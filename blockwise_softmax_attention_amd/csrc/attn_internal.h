@@ -65,6 +65,7 @@ hipError_t launch_preprocess(const KArgs& a, int dtype, int head_dim, hipStream_
 hipError_t launch_dq(const KArgs& a, int dtype, int head_dim, int cap, hipStream_t s);
 hipError_t launch_dkv(const KArgs& a, int dtype, int head_dim, int cap, hipStream_t s);
 hipError_t launch_reduce_heads(const float* x, float* out, int B, int H, int L, hipStream_t s);
+hipError_t launch_stream_probe(const void* src, long long bytes, int blocks, float* out, hipStream_t s);
 hipError_t launch_ranker_bounds(const int32_t* seg, int32_t* bounds, int B, int L, int32_t hist_id,
                                 int32_t cand_id, hipStream_t s);
 int fwd_key_tile(int dtype, int head_dim);   // keys per forward tile

@@ -157,6 +157,16 @@ attn_status attn_ranker_bounds(const int32_t* segment_ids, int32_t batch, int32_
                                int32_t history_id, int32_t candidate_id, int32_t* ranker_bounds,
                                void* stream);
 
+/* Measurement helper, not part of attention: the rate at which HBM feeds the
+ * direct-to-LDS, non-temporal 16-byte loads the kernels stream their tiles
+ * with.  blocks work-groups each read a contiguous bytes / blocks slice of src
+ * (device memory, 16-byte aligned) into LDS that nothing reads, and write one
+ * float per work-group to out (device memory, blocks floats, 4-byte aligned):
+ * the first float of the slice's last 1 KB.  ATTN_ERR_SHAPE unless
+ * 1 <= blocks <= 65536 and bytes is a positive multiple of 1024 * blocks.
+ * Nothing is allocated; the caller times the call on its stream. */
+attn_status attn_probe_stream(const void* src, int64_t bytes, int32_t blocks, float* out, void* stream);
+
 /* dK and dV (triton_kernels.py page, make_triton_backward_kernel_dkv), each
  * summed over the Hq/Hkv query heads of a key/value head inside one
  * workgroup (no atomics).  Writes dk, dv (B, L, Hkv, D). */

@@ -102,6 +102,14 @@ def test_null_and_misaligned_pointers_rejected_before_launch():
     assert lib.attn_bwd_dkv(ctypes.byref(cp), good, good, good, None, None, None, good, good, good,
                             good, good, None, None) == -1
     assert lib.attn_fwd(None, *ptrs, None) == -1
+    # the stream probe: shape and pointer checks, before any launch
+    assert lib.attn_probe_stream(good, 1 << 20, 0, good, None) == -2
+    assert lib.attn_probe_stream(good, 1 << 20, 65537, good, None) == -2
+    assert lib.attn_probe_stream(good, 1000 * 1024, 512, good, None) == -2   # not 1024 * blocks
+    assert lib.attn_probe_stream(good, 0, 1, good, None) == -2
+    assert lib.attn_probe_stream(None, 1 << 20, 4, good, None) == -1
+    assert lib.attn_probe_stream(good + 8, 1 << 20, 4, good, None) == -5
+    assert lib.attn_probe_stream(good, 1 << 20, 4, good + 2, None) == -5
 
 
 def test_status_strings():
