@@ -730,120 +730,208 @@ __global__ __launch_bounds__(NTHREADS, 2) void dq_bf16_kernel(KArgs a) {
 // ---------------------------------------------------------------------------
 // dQ from stored dS
 // ---------------------------------------------------------------------------
-// dQ^T += K^T dS^T over the visited key tiles of the workgroup's query tile,
+// dQ^T += K^T dS^T over the visited key tiles of two adjacent query tiles,
 // dS taken from the tiles the dK/dV kernel stored (WDS): no recomputation of
 // S, P or dP and no element work, so the kernel streams the stored tiles from
 // HBM.  Both operands reduce over keys and are read transposed from LDS
 // (ds_read_b64_tr_b16): the K tile (columns = d) and the dS tile in its
-// stored order (columns = queries; wave w takes its 32).
+// stored order (columns = queries; wave w of a half takes its 32).
 //
-// A step covers DQS_BN keys of one listed tile (the visited key tiles are
-// listed once per workgroup).  With 32-key steps the rings take 72.7 KB, so
-// two workgroups share a CU and one's wait, barrier and LDS latency hide
-// behind the other's MFMAs.  The dS stream gets the deeper ring: dS of step
-// n + DQS_SST - 1 and K of step n + 2 (K mostly hits L2) are loaded while
-// step n computes.  Every step issues the same loads in the same order (past
-// the last step the last one is fetched again into idle stages), so a single
-// vmcnt wait before the barrier finds both tiles of step n done: the loads
-// issued after K(n) are dS(n+SST-3), K(n+1) and dS(n+SST-2), and dS(n)
-// precedes K(n).  The dS tiles, read once, are loaded non-temporal (nt) so
-// that their stream does not push out of L2 the K tiles the XCD's other
-// workgroups read again (HBM bytes per launch on the long-context workload
-// 9.39 -> 8.83 GB fetched, 2% faster).
+// A work-group is eight waves: waves 0-3 hold query tile 2p, waves 4-7 tile
+// 2p + 1 of the same (batch row, query head), and the two halves share every
+// K tile.  The K loads cost per instruction, wherever they hit: in a
+// stand-alone copy of the load pattern on the long-context workload they took
+// 15% of the dS stream's time with one query tile per work-group and 4% with
+// two.  Two such work-groups fit a CU (about 74 KB of LDS each), so that one's
+// wait, barrier and LDS latency hide behind the other's MFMAs; with one
+// eight-wave work-group per CU the kernel was slower than with one query tile
+// per work-group.  The key tiles either half visits are listed once per
+// work-group, each entry with one visibility bit per half; a step covers
+// DQS_BN keys of one listed tile.  Every wave issues the same loads in the
+// same order at every step, so that one vmcnt wait before the barrier finds
+// the step's tiles done: a half that does not visit the step's tile loads
+// one of its own visited parts (or, without any, one of the other half's)
+// into its stage and skips its MFMAs.  Step n loads K of step n + 1 and dS
+// of step n + 2 (past the last step the last one is fetched again), so at
+// step n's wait only dS(n + 1) was issued after K(n).  A shallow ring is
+// enough: the dS stream alone reached the same rate with 3 stages as with
+// 8.  The dS tiles, read once, are loaded non-temporal so that their stream
+// does not push out of L2 the K tiles that are read again.
 #ifndef ATTN_DQS_BN
 #define ATTN_DQS_BN 32
 #endif
 constexpr int DQS_BN = ATTN_DQS_BN;               // keys per step (a part of a stored tile)
-constexpr int DQS_KST = 3;                        // K stages
-constexpr int DQS_SST = DQS_BN == 32 ? 5 : 6;     // dS stages
-constexpr int DQS_WG_PER_CU = DQS_BN == 32 ? 2 : 1;
+constexpr int DQS_KST = 2;                        // K stages
+constexpr int DQS_SST = 3;                        // dS stages (each: both halves)
+constexpr int DQS_NW = 2 * NWAVES;                // waves per work-group
+constexpr int DQS_THREADS = 64 * DQS_NW;
 constexpr int DQS_FLAGS = ATTN_MAX_SEQ_LEN_SEGMENTS / DS_T;
 
+// Work item -> (batch row, KV head, query head, query-tile pair p), with the
+// row order of decode_row_item (pairs in place of query tiles; causal pairs
+// longest first).
+struct PairItem {
+  int b, hkv, hq, p;
+};
+__device__ __forceinline__ PairItem decode_pair_item(const KArgs& a, int item, int P, const int* ord) {
+  PairItem it;
+  int rest;
+  if (ord != nullptr) {
+    const int R = a.n_items / 8, per_b = R / a.B, run = item / R, loc = item - run * R;
+    it.b = ord[loc / per_b];
+    rest = run * per_b + loc % per_b;
+  } else {
+    it.b = item % a.B;
+    rest = item / a.B;
+  }
+  const int g = rest % a.G;
+  rest /= a.G;
+  const int p_rev = rest % P;
+  it.hkv = rest / P;
+  it.p = a.causal ? (P - 1 - p_rev) : p_rev;
+  it.hq = it.hkv * a.G + g;
+  return it;
+}
+
 template <int D>
-__global__ __launch_bounds__(NTHREADS, DQS_WG_PER_CU) void dq_ds_bf16_kernel(KArgs a) {
+__global__ __launch_bounds__(DQS_THREADS, 2) void dq_ds_bf16_kernel(KArgs a) {
   constexpr int BN = DQS_BN, KST = DQS_KST, SST = DQS_SST, PARTS = DS_T / BN;
   constexpr int PSH = PARTS == 4 ? 2 : 1;   // log2(PARTS)
   static_assert(PARTS == 2 || PARTS == 4, "a stored tile splits into 2 or 4 steps");
-  using KT = BTile<BN, D, NWAVES>;
-  using ST = BTile<BN, DS_T, NWAVES>;
+  // waves that load K: all eight where the tile splits into eight 1 KB loads
+  constexpr int KNW = (BN * D * 2) / 1024 >= DQS_NW ? DQS_NW : NWAVES;
+  using KT = BTile<BN, D, KNW>;
+  using ST = BTile<BN, DS_T, NWAVES>;   // one half's part of a dS stage
   constexpr int NDB = D / 32, NK = KT::PER_WAVE, NS = ST::PER_WAVE;
-  static_assert(BM == DS_T, "a workgroup's query tile is one stored query tile");
-  static_assert(KST == 3 && SST >= 4, "load order of the two rings");
+  static_assert(BM == DS_T, "a half's query tile is one stored query tile");
+  static_assert(KST == 2 && SST == 3, "load order of the two rings");
+  static_assert(BN % 32 == 0 && ST::BYTES == BN * DS_T * 2, "dS load pattern");
 
   __shared__ __attribute__((aligned(1024))) char sK[KST][KT::BYTES];
-  __shared__ __attribute__((aligned(1024))) char sS[SST][ST::BYTES];
-  __shared__ unsigned char sFlag[DQS_FLAGS];
-  __shared__ unsigned char sFlag2[DQS_FLAGS];
-  __shared__ unsigned char sMixed[DQS_FLAGS];
-  __shared__ unsigned short sList[ATTN_MAX_SEQ_LEN / DS_T];   // visited key tiles - t_lo
-  __shared__ int sRange[3];
+  __shared__ __attribute__((aligned(1024))) char sS[SST][2][ST::BYTES];
+  __shared__ unsigned char sFlag[2][DQS_FLAGS];
+  __shared__ unsigned char sFlag2[2][DQS_FLAGS];
+  __shared__ unsigned char sMixed[2][DQS_FLAGS];
+  __shared__ unsigned short sList[ATTN_MAX_SEQ_LEN / DS_T];   // tile - t_min | visibility << 14
+  __shared__ int sRange[2][3];
+  __shared__ int sFirst1;
+  __shared__ int sOrd[64];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int half = wave >> 2, w4 = wave & 3;
   const int l32 = lane & 31, hh = lane >> 5;
   const int item = xcd_remap(blockIdx.x, gridDim.x);
   if (item >= a.n_items) return;
-  __shared__ int sOrd[64];
-  const RowItem it = decode_row_item(a, item, wave, l32, ranker_row_order(a, tid, sOrd) ? sOrd : nullptr);
-  const int L = a.L, b = it.b, qrow = it.qrow;
-  const int qt = it.q0 / DS_T;
+  const int P = (a.n_q_tiles + 1) / 2;
+  const PairItem it = decode_pair_item(a, item, P, ranker_row_order(a, tid, sOrd) ? sOrd : nullptr);
+  const int L = a.L, b = it.b;
 
   const long kv_rs = (long)a.Hkv * D;
   const uint32_t kv_rsb = (uint32_t)(kv_rs * sizeof(bf16));
-  const typename KT::Lane kln = KT::lane_of(kv_rsb, lane, wave);
+  const bool kload = wave < KNW;
+  const typename KT::Lane kln = KT::lane_of(kv_rsb, lane, kload ? wave : 0);
   const bf16* Kb = (const bf16*)a.k + ((long)b * L * a.Hkv + it.hkv) * D;
   const DsBand band = ds_band(L, a.causal, a.window);
-  const int t_lo = ds_lo(qt, band), t_hi = ds_hi(qt, band);
-  const bf16* Sb = (const bf16*)a.ds +
-                   (((long long)b * a.Hq + it.hq) * a.ds_slots + ds_offset(qt, band)) * DS_ELEMS;
-
   const MaskSpec ms = load_mask_spec(a, b);
   const bool has_seg = ms.has_seg;
   const int* segb = has_seg ? a.seg + (long)b * L : nullptr;
-  if (has_seg)
-    segment_flags(segb, it.q0, it.q1, t_lo, t_hi, DS_T, L, tid, sFlag, sMixed, sRange, sFlag2);
-  // The blocks the dK/dV kernel visited (and stored): the same tile class and
-  // symmetric segment test, evaluated from the query side once, by wave 0,
-  // into a compact list of key tiles (the loop then only indexes it).
+
+  // the two query tiles (the second may lie past the sequence)
+  int qtx[2], q0x[2], q1x[2], tlo[2], thi[2];
+#pragma unroll
+  for (int x = 0; x < 2; ++x) {
+    qtx[x] = 2 * it.p + x;
+    q0x[x] = qtx[x] * BM;
+    q1x[x] = imin(q0x[x] + BM, L);
+    const bool live = q0x[x] < L;
+    tlo[x] = live ? ds_lo(qtx[x], band) : 0;
+    thi[x] = live ? ds_hi(qtx[x], band) : 0;
+  }
+  const bool live1 = q0x[1] < L;
+  const int tmin = live1 ? imin(tlo[0], tlo[1]) : tlo[0];
+  const int tmax = live1 ? imax(thi[0], thi[1]) : thi[0];
+  if (has_seg) {
+#pragma unroll
+    for (int x = 0; x < 2; ++x)
+      if (x == 0 || live1)
+        segment_flags(segb, q0x[x], q1x[x], tmin, tmax, DS_T, L, tid, sFlag[x], sMixed[x], sRange[x],
+                      sFlag2[x]);
+  }
+  // The blocks the dK/dV kernel visited (and stored), per half: the same tile
+  // class and symmetric segment test, evaluated from the query side once, by
+  // wave 0, into a compact list of key tiles (the loop then only indexes it).
   if (wave == 0) {
-    int cnt = 0;
-    for (int t0 = t_lo; t0 < t_hi; t0 += 64) {
+    int cnt = 0, first0 = -1, first1 = -1;   // each half's first visited tile
+    for (int t0 = tmin; t0 < tmax; t0 += 64) {
       const int t = t0 + lane;
-      bool vis = t < t_hi &&
-                 tile_class(it.q0, it.q1, t * DS_T, t * DS_T + DS_T, ms) != TILE_EMPTY;
-      if (vis && has_seg) vis = sFlag[t - t_lo] && sFlag2[t - t_lo];
-      const uint64_t m = __ballot(vis);
+      int vis = 0;
+#pragma unroll
+      for (int x = 0; x < 2; ++x) {
+        bool v = t >= tlo[x] && t < thi[x] &&
+                 tile_class(q0x[x], q1x[x], t * DS_T, t * DS_T + DS_T, ms) != TILE_EMPTY;
+        if (v && has_seg) v = sFlag[x][t - tmin] && sFlag2[x][t - tmin];
+        vis |= v ? (1 << x) : 0;
+      }
+      const uint64_t m = __ballot(vis != 0);
+      const uint64_t m0 = __ballot(vis & 1), m1 = __ballot(vis & 2);
+      if (first0 < 0 && m0 != 0) first0 = t0 + __builtin_ctzll(m0);
+      if (first1 < 0 && m1 != 0) first1 = t0 + __builtin_ctzll(m1);
       const int pos = cnt + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
                                                            __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
-      if (vis) sList[pos] = (unsigned short)(t - t_lo);
+      if (vis != 0) sList[pos] = (unsigned short)((t - tmin) | (vis << 14));
       cnt += __builtin_popcountll(m);
     }
-    if (lane == 0) sRange[2] = cnt;
+    if (lane == 0) {
+      sRange[0][2] = cnt;
+      sRange[1][2] = first0;
+      sFirst1 = first1;
+    }
   }
   __syncthreads();
-  const int ntiles = sRange[2];
+  const int ntiles = sRange[0][2];
   // a step is one BN-key part of a listed tile; the parts of the sequence's
   // last tile that start at or past L are dropped
-  const int last = ntiles > 0 ? t_lo + sList[ntiles - 1] : 0;
+  const int last = ntiles > 0 ? tmin + (sList[ntiles - 1] & 0x3fff) : 0;
   const int last_parts = imin(PARTS, (L - last * DS_T + BN - 1) / BN);
   const int nsteps = ntiles > 0 ? PARTS * (ntiles - 1) + last_parts : 0;
-  // (e: the list entry of step n, sList[n >> PSH])
+
+  // this half's dS: its band's first slot, and a part it can always load (its
+  // first visited one, else the other half's first visited one)
+  const bf16* Sx[2];
+#pragma unroll
+  for (int x = 0; x < 2; ++x)
+    Sx[x] = (const bf16*)a.ds +
+            (((long long)b * a.Hq + it.hq) * a.ds_slots + (q0x[x] < L ? ds_offset(qtx[x], band) : 0)) *
+                DS_ELEMS;
+  const bf16* fb = nullptr;
+  if (nsteps > 0) {
+    const int first[2] = {sRange[1][2], sFirst1};
+    const int xs = first[half] >= 0 ? half : half ^ 1;
+    fb = Sx[xs] + (long long)(first[xs] - tlo[xs]) * DS_ELEMS;
+  }
+  const bf16* Sh = Sx[half];
+  const int tloh = tlo[half];
+
   auto issue_k = [&](int n, int stg, int e) {
-    const int kt = t_lo + e;
+    if (!kload) return;
+    const int kt = tmin + (e & 0x3fff);
     const int kr0 = kt * DS_T + (n & (PARTS - 1)) * BN;
 #pragma unroll
     for (int i = 0; i < NK; ++i)
       KT::issue_one(lds_offset(sK[stg]), Kb + (long)kr0 * kv_rs, kv_rsb, L - kr0, kln, wave, i);
   };
-  // The dS ring holds each step's BN keys (BN / 32 groups of the stored
-  // tile, contiguous) as stored: 1 KB loads, LDS image = global image.
-  static_assert(BN % 32 == 0 && ST::BYTES == BN * DS_T * 2, "dS load pattern");
+  // The dS ring holds each step's BN keys (BN / 32 groups of the stored tile,
+  // contiguous) as stored: 1 KB loads, LDS image = global image.
   auto issue_s = [&](int n, int stg, int e) {
-    const bf16* g = Sb + ((long)e * DS_ELEMS + (long)(n & (PARTS - 1)) * BN * DS_T);
+    const bool vis = (e >> (14 + half)) & 1;
+    const int kt = tmin + (e & 0x3fff);
+    const bf16* g = vis ? Sh + ((long long)(kt - tloh) * DS_ELEMS + (long long)(n & (PARTS - 1)) * BN * DS_T)
+                        : fb;
 #pragma unroll
     for (int i = 0; i < NS; ++i) {   // read once: non-temporal, K stays in L2
-      const uint32_t j = (uint32_t)(wave + NWAVES * i);
-      const uint32_t m0 = (uint32_t)__builtin_amdgcn_readfirstlane(lds_offset(sS[stg]) + j * 1024);
+      const uint32_t j = (uint32_t)(w4 + NWAVES * i);
+      const uint32_t m0 = (uint32_t)__builtin_amdgcn_readfirstlane(lds_offset(sS[stg][half]) + j * 1024);
       dma16_nt(uniform_ptr(g), j * 1024 + 16 * (uint32_t)lane, m0);
     }
   };
@@ -853,7 +941,7 @@ __global__ __launch_bounds__(NTHREADS, DQS_WG_PER_CU) void dq_ds_bf16_kernel(KAr
   // transposed reads (see BTile::tr_frag for the lane roles).
   auto ds_frag = [&](const char* lds, int t) -> bf16x8 {
     const int h = lane >> 5, mh = (lane >> 4) & 1, e = (lane & 15) >> 2, s = lane & 3;
-    const int c = 4 * wave + 2 * mh + (s >> 1);
+    const int c = 4 * w4 + 2 * mh + (s >> 1);
     const int r1 = 16 * t + 4 * h + e, r2 = r1 + 8;
     const int k1 = (r1 & ~31) | pi32(r1 & 31), k2 = (r2 & ~31) | pi32(r2 & 31);
     const char* a1 = lds + (k1 >> 5) * 8192 + ds_chunk_offset(k1 & 31, c) + ((s & 1) << 3);
@@ -870,36 +958,38 @@ __global__ __launch_bounds__(NTHREADS, DQS_WG_PER_CU) void dq_ds_bf16_kernel(KAr
   for (int i = 0; i < NDB; ++i) dqacc[i] = f32x16{};
 
   if (nsteps > 0) {
-    // prologue: dS(0 .. SST-4), K(0), dS(SST-3), K(1), dS(SST-2); step
-    // numbers past the last step repeat the last one
+    // prologue: dS(0), K(0), dS(1); step n loads K(n+1) and dS(n+2), so the
+    // only loads after K(n) at step n's wait are those of dS(n+1) (waves
+    // without K loads: the same); step numbers past the last step repeat the
+    // last one
     const int nl = nsteps - 1;
     auto entry = [&](int n) -> int { return sList[n >> PSH]; };
-#pragma unroll
-    for (int n = 0; n < SST - 3; ++n) issue_s(imin(n, nl), n, entry(imin(n, nl)));
+    issue_s(0, 0, entry(0));
     issue_k(0, 0, entry(0));
-    issue_s(imin(SST - 3, nl), SST - 3, entry(imin(SST - 3, nl)));
-    issue_k(imin(1, nl), 1, entry(imin(1, nl)));
-    issue_s(imin(SST - 2, nl), SST - 2, entry(imin(SST - 2, nl)));
+    issue_s(imin(1, nl), 1, entry(imin(1, nl)));
     // the list entries of the next step's loads, read one step ahead so that
     // their LDS latency passes during a step's MFMAs
-    int ek = entry(imin(2, nl)), es = entry(imin(SST - 1, nl));
+    int ek = entry(imin(1, nl)), es = entry(imin(2, nl));
     int ks = 0, ss = 0;   // stages of the current step
     for (int n = 0; n < nsteps; ++n) {
-      wait_vmcnt<2 * NS + NK>();
+      wait_vmcnt<NS>();
       __syncthreads();
-      issue_k(imin(n + 2, nl), ks == 0 ? 2 : ks - 1, ek);
-      issue_s(imin(n + SST - 1, nl), ss == 0 ? SST - 1 : ss - 1, es);
-      ek = entry(imin(n + 3, nl));
-      es = entry(imin(n + SST, nl));
-      const char* Kt = sK[ks];
-      const char* St = sS[ss];
+      const int ec = entry(n);
+      issue_k(imin(n + 1, nl), ks ^ 1, ek);
+      issue_s(imin(n + 2, nl), ss == 0 ? 2 : ss - 1, es);
+      ek = entry(imin(n + 2, nl));
+      es = entry(imin(n + 3, nl));
+      if ((ec >> (14 + half)) & 1) {
+        const char* Kt = sK[ks];
+        const char* St = sS[ss][half];
 #pragma unroll
-      for (int t = 0; t < BN / 16; ++t) {
-        const bf16x8 sf = ds_frag(St, t);
+        for (int t = 0; t < BN / 16; ++t) {
+          const bf16x8 sf = ds_frag(St, t);
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          const bf16x8 ka = KT::tr_frag(Kt, db, t, lane);
-          dqacc[db] = Elem<bf16>::mfma(ka, sf, dqacc[db]);
+          for (int db = 0; db < NDB; ++db) {
+            const bf16x8 ka = KT::tr_frag(Kt, db, t, lane);
+            dqacc[db] = Elem<bf16>::mfma(ka, sf, dqacc[db]);
+          }
         }
       }
       ks = ks + 1 == KST ? 0 : ks + 1;
@@ -908,6 +998,7 @@ __global__ __launch_bounds__(NTHREADS, DQS_WG_PER_CU) void dq_ds_bf16_kernel(KAr
     wait_vmcnt<0>();
   }
 
+  const int qrow = q0x[half] + 32 * w4 + l32;
   if (qrow < L) {
     float* drow = a.out0 + ((long)(b * L + qrow) * a.Hq + it.hq) * D;
 #pragma unroll
@@ -1510,9 +1601,12 @@ hipError_t launch_dkv_ds_bf16(const KArgs& a, int head_dim, int cap, hipStream_t
 }
 
 hipError_t launch_dq_ds_bf16(const KArgs& a, int head_dim, hipStream_t s) {
-  dim3 grid(a.n_items), block(NTHREADS);
-  if (head_dim == 64) hipLaunchKernelGGL((dq_ds_bf16_kernel<64>), grid, block, 0, s, a);
-  else hipLaunchKernelGGL((dq_ds_bf16_kernel<128>), grid, block, 0, s, a);
+  // one work-group per pair of query tiles (a.n_items counts query tiles)
+  KArgs c = a;
+  c.n_items = a.B * a.Hq * ((a.n_q_tiles + 1) / 2);
+  dim3 grid(c.n_items), block(DQS_THREADS);
+  if (head_dim == 64) hipLaunchKernelGGL((dq_ds_bf16_kernel<64>), grid, block, 0, s, c);
+  else hipLaunchKernelGGL((dq_ds_bf16_kernel<128>), grid, block, 0, s, c);
   return hipGetLastError();
 }
 
