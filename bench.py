@@ -44,14 +44,14 @@ HBM_GBPS = 8000.0
 KERNEL_SOURCES = ["attn_bf16.hip", "attn_bf16.h", "attn_device.h", "attn_tiles.h",
                   "attn_internal.h", "attn_bwd_common.h", "attn_preprocess.hip"]
 MEASURED_TRAFFIC = {
-    ("529d0ac48c0989ed", 5, 0): {"attn_fwd": (232048 * 2.0 + 134221) * 1024,
-                                 "attn_bwd_preprocess": (98333 * 2.0 + 4096) * 1024,
-                                 "attn_bwd_dkv_ds": (361786 * 2.0 + 8683520) * 1024,
-                                 "attn_bwd_dq_ds": (4313000 * 2.0 + 131079) * 1024},
-    ("529d0ac48c0989ed", 4, 0): {"attn_fwd": (171893 * 2.0 + 270336) * 1024,
-                                 "attn_bwd_preprocess": (196637 * 2.0 + 16404) * 1024,
-                                 "attn_bwd_dkv_ds": (1036245 * 2.0 + 6423047) * 1024,
-                                 "attn_bwd_dq_ds": (3210027 * 2.0 + 262162) * 1024},
+    ("bbfcd14174aa4bb4", 5, 0): {"attn_fwd": (237641 * 2.0 + 133989) * 1024,
+                                 "attn_bwd_preprocess": (98333 * 2.0 + 4097) * 1024,
+                                 "attn_bwd_dkv_ds": (362220 * 2.0 + 8683520) * 1024,
+                                 "attn_bwd_dq_ds": (4353492 * 2.0 + 131273) * 1024},
+    ("bbfcd14174aa4bb4", 4, 0): {"attn_fwd": (171941 * 2.0 + 270478) * 1024,
+                                 "attn_bwd_preprocess": (196638 * 2.0 + 16402) * 1024,
+                                 "attn_bwd_dkv_ds": (1036320 * 2.0 + 6423051) * 1024,
+                                 "attn_bwd_dq_ds": (3207965 * 2.0 + 262161) * 1024},
 }
 
 
