@@ -101,6 +101,32 @@ def test_segment_ids(layout):
     compare_paths(w, inp)
 
 
+@pytest.mark.parametrize("D", [64, 128])
+def test_query_tile_pairs_visit_different_key_tiles(D):
+    """The dQ kernel takes two adjacent 128-row query tiles per workgroup.
+    Segment boundaries at 384 and 512 make the tiles (2, 3) of one pair visit
+    disjoint key tiles ({0, 1, 2} and {3}); with L = 582 (five query tiles)
+    the last pair has no second tile."""
+    w = E(L=582, B=2, Hq=4, Hkv=2, D=D)
+    inp = make_inputs(w)
+    seg = np.zeros((w.B, w.L), dtype=np.int32)
+    seg[:, 384:512] = 1
+    seg[:, 512:] = 2
+    inp["segment_ids"] = torch.from_numpy(seg)
+    compare_paths(w, inp)
+
+
+def test_query_tile_pair_with_a_fully_masked_tile():
+    """Ranker bounds [0, 100, 100, 300] leave every row from 300 on without a
+    key: the pair (2, 3) has one query tile with visited key tiles and one
+    without any, the pair (4, 5) none at all."""
+    w = E(causal=False, L=700, Hq=2, Hkv=1, D=128)
+    inp = make_inputs(w)
+    inp["ranker_bounds"] = torch.tensor([[0, 100, 100, 300]], dtype=torch.int32)
+    got = compare_paths(w, inp)
+    assert np.all(got["dq"][0, 300:] == 0)
+
+
 def test_fully_masked_rows():
     # ranker bounds leave rows [0, 40) and [460, 500) outside both ranges
     w = E(causal=False, L=500, Hq=2, Hkv=1, D=128)
