@@ -38,17 +38,18 @@ HBM_GBPS = 8000.0
 # long-context and ranker workloads (default mode: single-bf16 dS, stored-dS
 # backward), scaled by what the same counters read for a plain 1 GiB device
 # copy (FETCH_SIZE x2.0, WRITE_SIZE x1.0); keyed by a hash of the kernel
-# sources they were taken on, so a changed kernel reports null.  Summary and
+# sources they were taken on, so a changed kernel reports null (the key was
+# moved once for an edit that left the device assembly byte-identical).  Summary and
 # commands: profiles/counters_long_context_causal_alsc_L32768.md and
 # profiles/kernel_trace_ranker_gqa_softsign_L8192.md.
 KERNEL_SOURCES = ["attn_bf16.hip", "attn_bf16.h", "attn_device.h", "attn_tiles.h",
                   "attn_internal.h", "attn_bwd_common.h", "attn_preprocess.hip"]
 MEASURED_TRAFFIC = {
-    ("bbfcd14174aa4bb4", 5, 0): {"attn_fwd": (237641 * 2.0 + 133989) * 1024,
+    ("be66c260ca48d300", 5, 0): {"attn_fwd": (237641 * 2.0 + 133989) * 1024,
                                  "attn_bwd_preprocess": (98333 * 2.0 + 4097) * 1024,
                                  "attn_bwd_dkv_ds": (362220 * 2.0 + 8683520) * 1024,
                                  "attn_bwd_dq_ds": (4353492 * 2.0 + 131273) * 1024},
-    ("bbfcd14174aa4bb4", 4, 0): {"attn_fwd": (171941 * 2.0 + 270478) * 1024,
+    ("be66c260ca48d300", 4, 0): {"attn_fwd": (171941 * 2.0 + 270478) * 1024,
                                  "attn_bwd_preprocess": (196638 * 2.0 + 16402) * 1024,
                                  "attn_bwd_dkv_ds": (1036320 * 2.0 + 6423051) * 1024,
                                  "attn_bwd_dq_ds": (3207965 * 2.0 + 262161) * 1024},

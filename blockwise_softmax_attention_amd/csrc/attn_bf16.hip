@@ -757,10 +757,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void dq_bf16_kernel(KArgs a) {
 // enough: the dS stream alone reached the same rate with 3 stages as with
 // 8.  The dS tiles, read once, are loaded non-temporal so that their stream
 // does not push out of L2 the K tiles that are read again.
-#ifndef ATTN_DQS_BN
-#define ATTN_DQS_BN 32
-#endif
-constexpr int DQS_BN = ATTN_DQS_BN;               // keys per step (a part of a stored tile)
+constexpr int DQS_BN = 32;                        // keys per step (a quarter of a stored tile)
 constexpr int DQS_KST = 2;                        // K stages
 constexpr int DQS_SST = 3;                        // dS stages (each: both halves)
 constexpr int DQS_NW = 2 * NWAVES;                // waves per work-group
