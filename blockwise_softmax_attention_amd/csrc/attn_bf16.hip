@@ -848,6 +848,9 @@ __global__ __launch_bounds__(DQS_THREADS, 2) void dq_ds_bf16_kernel(KArgs a) {
   const bool live1 = q0x[1] < L;
   const int tmin = live1 ? imin(tlo[0], tlo[1]) : tlo[0];
   const int tmax = live1 ? imax(thi[0], thi[1]) : thi[0];
+  // (segment_flags strides by NTHREADS: the threads past it repeat writes of
+  // the same flag values, and only the first BM threads take part in the id
+  // range, so the 512-thread work-group computes the same tables)
   if (has_seg) {
 #pragma unroll
     for (int x = 0; x < 2; ++x)
